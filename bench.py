@@ -1,0 +1,246 @@
+"""Benchmark of the sink-attention hot path on one MI355X.
+
+One step = one pass over every stage of the path on its synthetic workload:
+  prefill  causal prefill, bf16, B=4 x 2048, Hq=64, Hkv=8, D=64      (MFMA-bound)
+  decode   paged decode, bf16, B=64, kv_len U[512,8192], + merge     (HBM-bound)
+  split    split-KV decode, bf16, B=4, kv_len 131072, 64 splits, + merge (HBM-bound)
+`value` is the prefill throughput in TFLOP/s (algorithmic flops: 4*D per
+causal-visible (query, key) pair) from HIP events around the prefill launch
+on the stream it runs on; the decode stages report achieved HBM GB/s.  The
+256 MB last-level cache is flushed (1 GiB write) before each decode stage,
+outside the kernel events.  The fp64 CPU oracle is timed on a bounded sample
+of the prefill workload as a reported baseline (rank 0, N=1 only).
+
+Prints one JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def prefill_flops(lens_q, lens_kv, hq, dim, causal=True):
+    pairs = 0
+    for lq, lkv in zip(lens_q, lens_kv):
+        if causal:
+            shift = lkv - lq
+            # row i sees min(lkv, max(0, i + shift + 1)) keys
+            for i in range(lq):
+                pairs += min(lkv, max(0, i + shift + 1))
+        else:
+            pairs += lq * lkv
+    return 4.0 * dim * pairs * hq
+
+
+def decode_bytes(kv_lens, hq, hkv, dim, splits, es=2):
+    """Algorithmic HBM bytes of paged decode (+ merge when splits > 1)."""
+    tokens = sum(int(L) for L in kv_lens)
+    kv = tokens * hkv * dim * 2 * es                      # K and V of valid tokens
+    b = len(kv_lens)
+    q_o = 2 * b * hq * dim * es                           # q read, output written
+    pages = sum((int(L) + 15) // 16 for L in kv_lens) * 4  # page-table entries
+    partials = b * hq * splits * (dim + 2) * 4 if splits > 1 else 0
+    decode = kv + b * hq * dim * es + pages + partials    # decode kernel
+    merge = partials + b * hq * dim * es if splits > 1 else 0
+    return dict(total=kv + q_o + pages + 2 * partials, decode=decode, merge=merge, kv=kv)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle baseline sample")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only; run with --gpus 1 "
+              "(the multi-GPU split of this path is described, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gqa_attention_sinks_initialised_amd as attn
+    import workloads
+
+    attn.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ---- inputs (seeded, synthetic), resident in HBM before timing
+    c2 = workloads.workload(2, device=dev)
+    c3 = workloads.workload(3, device=dev, cache_device=dev)
+    c4 = workloads.workload(4, device=dev, cache_device=dev)
+    s3 = attn.default_num_splits(c3["kv_lens"].tolist(), 8)
+    s4 = 64
+    out2 = torch.empty_like(c2["q"])
+    hq = 64
+
+    def mk_partials(b, s):
+        f = dict(device=dev, dtype=torch.float32)
+        return (torch.empty((b, hq, s), **f), torch.empty((b, hq, s), **f),
+                torch.empty((b, hq, s, 64), **f))
+
+    p3, p4 = mk_partials(64, s3), mk_partials(4, s4)
+    o3 = torch.empty((64, hq, 64), device=dev, dtype=torch.bfloat16)
+    o4 = torch.empty((4, hq, 64), device=dev, dtype=torch.bfloat16)
+    flush = torch.empty(1 << 30, device=dev, dtype=torch.uint8)
+
+    def run_prefill():
+        attn.attn_sink_prefill(c2["q"], c2["k"], c2["v"], c2["sinks"], c2["cu_seqlens_q"],
+                               c2["cu_seqlens_kv"], 2048, 8, c2["sm_scale"], True, out=out2)
+
+    def run_decode(c, s, parts, out, ev=None):
+        attn.attn_sink_decode_paged(c["q"], c["k_cache"], c["v_cache"], c["page_table"],
+                                    c["kv_lens"], c["sinks"], 8, c["sm_scale"], s,
+                                    partial_m=parts[0], partial_d=parts[1],
+                                    partial_o=parts[2])
+        if ev is not None:
+            ev.record()
+        attn.attn_sink_merge(*parts, out=out)
+
+    names = ["prefill", "decode", "decode_merge", "split", "split_merge"]
+
+    def step(evs=None):
+        e = evs or {}
+        if evs: e["t0"].record()
+        run_prefill()
+        if evs: e["t1"].record()
+        flush.fill_(1)
+        if evs: e["t2"].record()
+        run_decode(c3, s3, p3, o3, e.get("t3"))
+        if evs: e["t4"].record()
+        flush.fill_(2)
+        if evs: e["t5"].record()
+        run_decode(c4, s4, p4, o4, e.get("t6"))
+        if evs: e["t7"].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [{k: torch.cuda.Event(enable_timing=True) for k in
+            ("t0", "t1", "t2", "t3", "t4", "t5", "t6", "t7")} for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+
+    def avg_ms(a, b):
+        return sum(e[a].elapsed_time(e[b]) for e in evs) / len(evs)
+
+    t = dict(prefill=avg_ms("t0", "t1"), decode=avg_ms("t2", "t3"),
+             decode_merge=avg_ms("t3", "t4"), split=avg_ms("t5", "t6"),
+             split_merge=avg_ms("t6", "t7"))
+
+    fl2 = prefill_flops(c2["lens_q"], c2["lens_kv"], hq, 64)
+    tflops = fl2 / (t["prefill"] * 1e-3) / 1e12
+    b3 = decode_bytes(c3["kv_lens"].tolist(), hq, 8, 64, s3)
+    b4 = decode_bytes(c4["kv_lens"].tolist(), hq, 8, 64, s4)
+    gbs3 = b3["total"] / ((t["decode"] + t["decode_merge"]) * 1e-3) / 1e9
+    gbs4 = b4["total"] / ((t["split"] + t["split_merge"]) * 1e-3) / 1e9
+    gbs3_k = b3["decode"] / (t["decode"] * 1e-3) / 1e9
+    gbs4_k = b4["decode"] / (t["split"] * 1e-3) / 1e9
+
+    result = {
+        "metric": "prefill attention TFLOP/s (bf16) + decode KV-read HBM GB/s, % of roofline",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) q/k/v, N(0,2) sinks; random page placement)",
+        "config": {"workload": "causal prefill bf16 B=4 x 2048, Hq=64 Hkv=8 D=64 "
+                               "(+ per step: paged decode B=64 len U[512,8192]; split-KV "
+                               "decode B=4 len 131072 x 64 splits)",
+                   "prefill_tokens": 8192, "decode_splits": s3, "split_splits": s4},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "prefill_kernel<bf16>", "flops_per_launch": fl2,
+                     "us_per_launch": round(t["prefill"] * 1e3, 2)},
+        "decode": {"workload": c3["name"], "splits": s3,
+                   "us_decode": round(t["decode"] * 1e3, 2),
+                   "us_merge": round(t["decode_merge"] * 1e3, 2),
+                   "bytes": b3["total"], "GB/s": round(gbs3, 1),
+                   "frac": round(gbs3 / PEAK_HBM_GBS, 4),
+                   "decode_kernel_GB/s": round(gbs3_k, 1),
+                   "decode_kernel_frac": round(gbs3_k / PEAK_HBM_GBS, 4)},
+        "split_decode": {"workload": c4["name"], "splits": s4,
+                         "us_decode": round(t["split"] * 1e3, 2),
+                         "us_merge": round(t["split_merge"] * 1e3, 2),
+                         "bytes": b4["total"], "GB/s": round(gbs4, 1),
+                         "frac": round(gbs4 / PEAK_HBM_GBS, 4),
+                         "decode_kernel_GB/s": round(gbs4_k, 1),
+                         "decode_kernel_frac": round(gbs4_k / PEAK_HBM_GBS, 4)},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(c2, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(c2, target_s):
+    """The fp64 oracle on a bounded sample of the prefill workload: every head
+    of a set of query tokens spread evenly over the four sequences."""
+    import numpy as np
+    import oracle
+
+    host = {k: (v.cpu() if hasattr(v, "cpu") else v) for k, v in c2.items()}
+    hq, lens = 64, host["lens_q"]
+
+    def rows_for(n_tok):
+        toks = []
+        off = 0
+        for L in lens:
+            toks += list(off + np.linspace(0, L - 1, n_tok // len(lens)).astype(np.int64))
+            off += L
+        toks = np.repeat(np.array(toks, dtype=np.int64), hq)
+        heads = np.tile(np.arange(hq, dtype=np.int32), len(toks) // hq)
+        return toks, heads
+
+    def flops_of(toks):
+        cu = np.array(host["cu_seqlens_q"].tolist())
+        seq = np.searchsorted(cu, toks, side="right") - 1
+        i = toks - cu[seq]
+        return float(np.sum(4.0 * 64 * (i + 1)))   # Lq == Lkv: row i sees i+1 keys
+
+    n_tok = 16
+    toks, heads = rows_for(n_tok)
+    t0 = time.perf_counter()
+    oracle.prefill(host["q"], host["k"], host["v"], host["sinks"], host["cu_seqlens_q"],
+                   host["cu_seqlens_kv"], 8, 8, host["sm_scale"], True, rows=(toks, heads))
+    dt = time.perf_counter() - t0
+    scale = max(1, int(target_s / max(dt, 1e-3)))
+    n_tok = min(2048, n_tok * scale)
+    toks, heads = rows_for(n_tok)
+    t0 = time.perf_counter()
+    oracle.prefill(host["q"], host["k"], host["v"], host["sinks"], host["cu_seqlens_q"],
+                   host["cu_seqlens_kv"], 8, 8, host["sm_scale"], True, rows=(toks, heads))
+    dt = time.perf_counter() - t0
+    fl = flops_of(toks)
+    return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": "%d query tokens x 64 heads of the prefill workload (evenly spaced over "
+                      "the 4 sequences), %.3g GFLOP algorithmic, %.1f s" % (
+                          len(toks) // hq, fl / 1e9, dt)}
+
+
+if __name__ == "__main__":
+    main()

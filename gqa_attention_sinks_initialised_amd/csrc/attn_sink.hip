@@ -1,0 +1,856 @@
+// attn_sink.hip -- gfx950 (MI355X) kernels and C ABI for grouped-query
+// attention with per-head attention sinks.
+//
+// The operation (page "GPT-OSS on Day 0", perplexity.ai, sections
+// "Attention: GQA with Attention Sinks" and "Kernels for GPT-OSS / Sink
+// Attention"): each query head h owns a sink logit s_h that joins the softmax
+// denominator and has no value row; query head h reads key/value head
+// h / G.  The softmax runs online: a running max m that starts at the head's
+// sink (not at -inf) and a running sum d that starts at e^(s - m) = 1, so the
+// sink is accumulated exactly once.  The work is spread over heads and over
+// blocks of the key length; when the key range is split, only the first
+// block starts from the sink, and a merge combines the blocks' (m, d, o).
+//
+// Kernels (all hand-written for CDNA4, 64-lane wavefronts):
+//   decode_kernel   paged decode, one query token per sequence.  One
+//                   workgroup owns (sequence, kv head, key chunk); the G query
+//                   heads of the group sit in the 16 columns of one MFMA tile,
+//                   so every K and V page is loaded from HBM once for all of
+//                   them.  K and V fragments go straight from HBM into MFMA
+//                   operands (no LDS staging); pages are read with 16-byte
+//                   (K) and 8-byte (V) vector loads.  The V page is stored
+//                   dim-major so that the P.V contraction (over tokens) reads
+//                   contiguous memory.
+//   merge_kernel    split-KV merge of (m, d, o) partial states.
+//   prefill_kernel  ragged (causal) prefill.  One workgroup owns a tile of
+//                   query tokens x all G heads of one kv head (4 waves x 64
+//                   rows), so a K/V tile staged in LDS serves every head of
+//                   the group.  S^T = K Q^T and O^T = V^T P^T run on 32x32
+//                   MFMAs; the transposed products make the score tile's
+//                   register layout directly usable as the P operand of the
+//                   next product, and keep each query row's softmax state in
+//                   the lane that owns that row.
+//
+// Internally logits are kept in log2 units (x * sm_scale * log2 e) so the
+// exponentials are single v_exp_f32 instructions; the sink is converted by
+// log2 e only (it is not multiplied by sm_scale).
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "attn_sink.h"
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr int kHeadDim = 64;
+constexpr int kPage = 16;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+enum { DT_F32 = ATTN_SINK_F32, DT_BF16 = ATTN_SINK_BF16 };
+
+// ------------------------------------------------------------------ helpers
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float xor_max(float v, int mask) {
+  return fmaxf(v, __shfl_xor(v, mask, 64));
+}
+
+__device__ __forceinline__ float xor_sum(float v, int mask) {
+  return v + __shfl_xor(v, mask, 64);
+}
+
+// fp32 -> bf16 bits, round to nearest even (hardware conversion on gfx950).
+__device__ __forceinline__ unsigned short to_bf16(float x) {
+  return __builtin_bit_cast(unsigned short, static_cast<__bf16>(x));
+}
+
+__device__ __forceinline__ unsigned int pack_bf16x2(float lo, float hi) {
+  return (unsigned int)to_bf16(lo) | ((unsigned int)to_bf16(hi) << 16);
+}
+
+__device__ __forceinline__ float bf16_lo(unsigned int w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(unsigned int w) { return __uint_as_float(w & 0xffff0000u); }
+
+template <typename V>
+__device__ __forceinline__ V ld_global(const void* p) {
+  return *reinterpret_cast<const V*>(p);
+}
+
+// Raw buffer resource over [base, base + bytes): loads past the end return
+// zero and stores past the end are dropped, which is how ragged sequence
+// tails are handled without branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+__device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+// ============================================================ decode kernel
+//
+// Work item = (key chunk c, kv head, sequence b); WAVES waves share it by
+// taking every WAVES-th page of the chunk, then merge their states in LDS.
+// Per wave and page (16 tokens) the tile maths is
+//   S^T[16 tok x 16 heads] = K[16 tok x 64] . Q^T[64 x 16 heads]
+//   O^T[64 x 16 heads]    += V^T[64 x 16 tok] . P^T[16 tok x 16 heads]
+// Register layout of a 16x16 MFMA result: lane l holds column l%16 (the
+// head) and rows 4*(l/16) + r, r = 0..3 (tokens for S^T, dims for O^T), so
+// each lane's softmax state belongs to exactly one head.
+
+template <int DT>
+struct DecodeFrag;
+
+template <>
+struct DecodeFrag<DT_BF16> {
+  u32x4 k[2];  // K[token l%16][32s + 8g .. +7], s = 0, 1
+  u32x2 v[4];  // Vt[16j + l%16][4g .. 4g+3], j = 0..3
+};
+
+template <>
+struct DecodeFrag<DT_F32> {
+  u32x4 k[4];  // K[token l%16][16g .. 16g+15]
+  u32x4 v[4];  // Vt[16j + l%16][4g .. 4g+3]
+};
+
+template <int DT, int WAVES, int UNROLL>
+__global__ __launch_bounds__(64 * WAVES) void decode_kernel(
+    const char* __restrict__ q, const char* __restrict__ kc, const char* __restrict__ vc,
+    const int32_t* __restrict__ page_table, const int32_t* __restrict__ kv_lens,
+    const float* __restrict__ sinks, int max_pages, int num_pages, int hkv, int group,
+    float qk_scale_log2, int splits, float* __restrict__ part_m, float* __restrict__ part_d,
+    float* __restrict__ part_o, char* __restrict__ out) {
+  constexpr int ES = DT == DT_BF16 ? 2 : 4;  // element size
+  constexpr size_t kPageElems = (size_t)kPage * kHeadDim;
+  const int c = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int hq = hkv * group;
+  const bool head_ok = n < group;
+  const int h = kvh * group + (head_ok ? n : 0);
+
+  const int L = clampi(kv_lens[b], 0, max_pages * kPage);
+  const int np = (L + kPage - 1) / kPage;
+  const int ppc = (np + splits - 1) / splits;
+  const int p_begin = min(c * ppc, np);
+  const int p_end = min(p_begin + ppc, np);
+
+  // Q^T operand (B of S^T = K Q^T): this lane's head n, its k-slice of dims.
+  const char* qrow = q + ((size_t)b * hq + h) * kHeadDim * ES;
+  u32x4 qf[DT == DT_BF16 ? 2 : 4];
+  if constexpr (DT == DT_BF16) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      qf[s] = head_ok ? ld_global<u32x4>(qrow + (32 * s + 8 * g) * ES) : u32x4{0, 0, 0, 0};
+  } else {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      qf[s] = head_ok ? ld_global<u32x4>(qrow + (16 * g + 4 * s) * ES) : u32x4{0, 0, 0, 0};
+  }
+
+  // Running state.  Chunk 0's first wave starts from the sink: m = s (log2
+  // units), d = e^(s - m) = 1 (0 when s = -inf), counted in lane group 0 only
+  // because d is summed over the four lane groups at the end.
+  const float sink = head_ok ? sinks[h] : kNegInf;
+  const bool carries_sink = (c == 0) && (w == 0);
+  float m_run = carries_sink ? sink * kLog2e : kNegInf;
+  float d_run = (carries_sink && g == 0 && sink != kNegInf) ? 1.0f : 0.0f;
+  f32x4 o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int32_t* pt = page_table + (size_t)b * max_pages;
+  const size_t head_page_stride = kPageElems * ES;  // bytes per (page, kv head)
+
+  auto load_page = [&](int phys, DecodeFrag<DT>& f) {
+    const char* kp = kc + ((size_t)phys * hkv + kvh) * head_page_stride;
+    const char* vp = vc + ((size_t)phys * hkv + kvh) * head_page_stride;
+    if constexpr (DT == DT_BF16) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        f.k[s] = ld_global<u32x4>(kp + ((size_t)n * kHeadDim + 32 * s + 8 * g) * ES);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        f.v[j] = ld_global<u32x2>(vp + ((size_t)(16 * j + n) * kPage + 4 * g) * ES);
+    } else {
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        f.k[s] = ld_global<u32x4>(kp + ((size_t)n * kHeadDim + 16 * g + 4 * s) * ES);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        f.v[j] = ld_global<u32x4>(vp + ((size_t)(16 * j + n) * kPage + 4 * g) * ES);
+    }
+  };
+
+  auto compute_page = [&](DecodeFrag<DT>& f, int p) {
+    // S^T tile
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (DT == DT_BF16) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, f.k[t]),
+                                                    __builtin_bit_cast(bf16x8, qf[t]), s, 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int t = 0; t < 16; ++t)
+        s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(f.k[t >> 2][t & 3]),
+                                                 __uint_as_float(qf[t >> 2][t & 3]), s, 0, 0, 0);
+    }
+    // tokens 4g + r of this page; mask the tail of the last page
+    const int valid = L - (p * kPage + 4 * g);  // tokens of this lane group still < L
+    float x[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) x[r] = (r < valid) ? s[r] * qk_scale_log2 : kNegInf;
+    if (valid < 4) {  // zero V of masked tokens so NaN/Inf junk in the slots cannot leak
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (DT == DT_BF16) {
+          unsigned int lo = f.v[j][0], hi = f.v[j][1];
+          if (valid < 1) lo &= 0xffff0000u;
+          if (valid < 2) lo &= 0x0000ffffu;
+          if (valid < 3) hi &= 0xffff0000u;
+          hi &= 0x0000ffffu;
+          f.v[j][0] = lo;
+          f.v[j][1] = hi;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (r >= valid) f.v[j][r] = 0u;
+        }
+      }
+    }
+    float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    mx = xor_max(mx, 16);
+    mx = xor_max(mx, 32);
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    float pv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pv[r] = fast_exp2(x[r] - m_use);
+    d_run = d_run * alpha + ((pv[0] + pv[1]) + (pv[2] + pv[3]));
+    m_run = m_new;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] *= alpha;
+    if constexpr (DT == DT_BF16) {
+      const i16x4 pb = __builtin_bit_cast(
+          i16x4, u32x2{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])});
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        o[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, f.v[j]), pb,
+                                                         o[j], 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          o[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(f.v[j][r]), pv[r], o[j], 0,
+                                                      0, 0);
+    }
+  };
+
+  // Page walk: this wave takes pages p_begin + w, + WAVES, ...; UNROLL pages
+  // are loaded before any is consumed so several loads are in flight.
+  int p = p_begin + w;
+  for (; p + (UNROLL - 1) * WAVES < p_end; p += UNROLL * WAVES) {
+    DecodeFrag<DT> f[UNROLL];
+    int phys[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      phys[u] = __builtin_amdgcn_readfirstlane(pt[p + u * WAVES]);
+      if ((unsigned)phys[u] < (unsigned)num_pages) load_page(phys[u], f[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u)
+      if ((unsigned)phys[u] < (unsigned)num_pages) compute_page(f[u], p + u * WAVES);
+  }
+  for (; p < p_end; p += WAVES) {
+    DecodeFrag<DT> f;
+    const int phys = __builtin_amdgcn_readfirstlane(pt[p]);
+    if ((unsigned)phys < (unsigned)num_pages) {
+      load_page(phys, f);
+      compute_page(f, p);
+    }
+  }
+
+  // Combine lane groups, then the waves of the workgroup (same merge rule as
+  // the split merge; only one state carries the sink).
+  d_run = xor_sum(d_run, 16);
+  d_run = xor_sum(d_run, 32);
+  __shared__ float sm_m[WAVES][16], sm_d[WAVES][16];
+  __shared__ float sm_o[WAVES][16][kHeadDim + 4];
+  if (g == 0) {
+    sm_m[w][n] = m_run;
+    sm_d[w][n] = d_run;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sm_o[w][n][16 * j + 4 * g + r] = o[j][r];
+  __syncthreads();
+
+  for (int idx = threadIdx.x; idx < 16 * 16; idx += 64 * WAVES) {
+    const int hh = idx >> 4, d0 = (idx & 15) * 4;
+    if (hh >= group) continue;
+    float M = kNegInf;
+#pragma unroll
+    for (int ww = 0; ww < WAVES; ++ww) M = fmaxf(M, sm_m[ww][hh]);
+    float D = 0.f, O[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ww = 0; ww < WAVES; ++ww) {
+      const float mw = sm_m[ww][hh];
+      const float e = (mw == kNegInf) ? 0.f : fast_exp2(mw - M);
+      D += sm_d[ww][hh] * e;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) O[i] += sm_o[ww][hh][d0 + i] * e;
+    }
+    const int head = kvh * group + hh;
+    const size_t row = (size_t)b * hq + head;
+    if (splits == 1) {
+      float y[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) y[i] = D > 0.f ? O[i] / D : 0.f;
+      if constexpr (DT == DT_BF16) {
+        *reinterpret_cast<u32x2*>(out + (row * kHeadDim + d0) * 2) =
+            u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+      } else {
+        *reinterpret_cast<f32x4*>(out + (row * kHeadDim + d0) * 4) = f32x4{y[0], y[1], y[2], y[3]};
+      }
+    } else {
+      const size_t st = row * splits + c;
+      if (d0 == 0) {
+        part_m[st] = (M == kNegInf) ? kNegInf : M * kLn2;
+        part_d[st] = D;
+      }
+      *reinterpret_cast<f32x4*>(part_o + st * kHeadDim + d0) = f32x4{O[0], O[1], O[2], O[3]};
+    }
+  }
+}
+
+// ============================================================= merge kernel
+//
+// One wave per (sequence, query head) row; lane = output dim.  Split states
+// are read 64 at a time (lane c holds chunk c's m and d), their weights
+// e^(m_c - M) are formed once per chunk and broadcast across the wave.
+
+template <int DT>
+__global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pm,
+                                                    const float* __restrict__ pd,
+                                                    const float* __restrict__ po, int rows,
+                                                    int splits, char* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const float* m = pm + (size_t)row * splits;
+  const float* d = pd + (size_t)row * splits;
+  const float* o = po + (size_t)row * splits * kHeadDim;
+  float M = kNegInf;
+  for (int c = lane; c < splits; c += 64) M = fmaxf(M, m[c]);
+#pragma unroll
+  for (int k = 1; k < 64; k <<= 1) M = xor_max(M, k);
+  float D = 0.f, O = 0.f;
+  for (int c0 = 0; c0 < splits; c0 += 64) {
+    const int c = c0 + lane;
+    const float mc = c < splits ? m[c] : kNegInf;
+    const float wc = (mc == kNegInf) ? 0.f : fast_exp2((mc - M) * kLog2e);
+    D += (c < splits ? d[c] : 0.f) * wc;
+    const int nc = min(64, splits - c0);
+    for (int i = 0; i < nc; ++i) {
+      const float wi = __shfl(wc, i, 64);
+      O += wi * o[(size_t)(c0 + i) * kHeadDim + lane];
+    }
+  }
+#pragma unroll
+  for (int k = 1; k < 64; k <<= 1) D = xor_sum(D, k);
+  const float y = D > 0.f ? O / D : 0.f;
+  if constexpr (DT == DT_BF16) {
+    reinterpret_cast<unsigned short*>(out)[(size_t)row * kHeadDim + lane] = to_bf16(y);
+  } else {
+    reinterpret_cast<float*>(out)[(size_t)row * kHeadDim + lane] = y;
+  }
+}
+
+// =========================================================== prefill kernel
+//
+// Workgroup = 4 waves; wave w owns 64 rows, row r = (token r / G, head r % G)
+// of tokens [t_begin + w*TW, +TW), TW = 64 / G.  Key tiles of 64 are staged
+// in LDS (K row-major, V transposed to dim-major) with a double buffer: the
+// next tile's global loads are in flight while the current tile is used.
+// Per tile and wave:
+//   S^T[64 keys x 64 rows]  = K . Q^T       (2 key blocks x 2 row blocks)
+//   O^T[64 dims x 64 rows] += V^T . P^T     (2 dim blocks x 2 row blocks)
+// A 32x32 MFMA result gives lane l column l%32 (a row) and the 16 rows
+// 8*(r/4) + 4*(l/32) + r%4, r = 0..15 (keys for S^T, dims for O^T).  Each
+// row's 64 keys are thus split over lanes l and l^32; its max is one
+// cross-lane exchange and its sum is deferred to the end.
+
+template <int DT>
+struct PrefillCfg;
+
+template <>
+struct PrefillCfg<DT_BF16> {
+  static constexpr int ES = 2;
+  static constexpr int KROW = kHeadDim + 8;  // elements per LDS K row (pad 16 B)
+  static constexpr int VROW = 64 + 4;        // elements per LDS Vt row (pad 8 B)
+  static constexpr int MIN_BLOCKS = 2;
+};
+
+template <>
+struct PrefillCfg<DT_F32> {
+  static constexpr int ES = 4;
+  static constexpr int KROW = kHeadDim + 4;
+  static constexpr int VROW = 64 + 4;
+  static constexpr int MIN_BLOCKS = 1;
+};
+
+template <int DT>
+__global__ __launch_bounds__(256, PrefillCfg<DT>::MIN_BLOCKS) void prefill_kernel(
+    const char* __restrict__ q, const char* __restrict__ k, const char* __restrict__ v,
+    const float* __restrict__ sinks, const int32_t* __restrict__ cu_q,
+    const int32_t* __restrict__ cu_kv, int total_q, int total_kv, int hkv, int group,
+    float qk_scale_log2, int causal, int n_qtiles, char* __restrict__ out) {
+  using Cfg = PrefillCfg<DT>;
+  constexpr int ES = Cfg::ES, KROW = Cfg::KROW, VROW = Cfg::VROW;
+  constexpr int BK = 64;  // keys per tile
+  __shared__ __attribute__((aligned(16))) char lds_k[2][BK * KROW * ES];
+  __shared__ __attribute__((aligned(16))) char lds_v[2][kHeadDim * VROW * ES];
+
+  const int b = blockIdx.z, kvh = blockIdx.y;
+  const int tile = n_qtiles - 1 - (int)blockIdx.x;  // longest causal tiles first
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, col = lane & 31;
+  const int hq = hkv * group;
+  const int TW = 64 / group;  // tokens per wave
+  const int TB = 4 * TW;      // tokens per workgroup
+
+  const int q0 = clampi(cu_q[b], 0, total_q), q1 = clampi(cu_q[b + 1], q0, total_q);
+  const int k0 = clampi(cu_kv[b], 0, total_kv), k1 = clampi(cu_kv[b + 1], k0, total_kv);
+  const int Lq = q1 - q0, Lkv = k1 - k0;
+  const int t_begin = tile * TB;
+  if (t_begin >= Lq) return;
+  const int t_last = min(t_begin + TB, Lq) - 1;
+  const int shift = Lkv - Lq;  // bottom-right causal alignment
+
+  // keys this workgroup needs, and the first tile that needs masking
+  int n_keys = causal ? min(Lkv, t_last + shift + 1) : Lkv;
+  n_keys = max(n_keys, 0);
+  const int n_tiles = (n_keys + BK - 1) / BK;
+  const int lim_min = causal ? min(t_begin + shift, Lkv - 1) : Lkv - 1;
+
+  // ---- rows of this lane: rb = 0, 1
+  int lim[2], head[2], tok[2];
+  bool valid[2];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int r = 32 * rb + col;
+    const int tl = r / group, hl = r - tl * group;
+    tok[rb] = t_begin + w * TW + tl;
+    head[rb] = kvh * group + hl;
+    valid[rb] = (tl < TW) && (tok[rb] < Lq);
+    lim[rb] = valid[rb] ? (causal ? min(tok[rb] + shift, Lkv - 1) : Lkv - 1) : -1;
+  }
+
+  // ---- Q^T operand: lane group g owns dims [32g, 32g+32)
+  const __amdgpu_buffer_rsrc_t qr =
+      make_rsrc(q + (size_t)q0 * hq * kHeadDim * ES, (uint32_t)((size_t)Lq * hq * kHeadDim * ES));
+  constexpr int QV = DT == DT_BF16 ? 4 : 8;  // 16-byte vectors per lane per row
+  u32x4 qf[2][QV];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const uint32_t base = ((uint32_t)tok[rb] * hq + head[rb]) * kHeadDim * ES + 32 * g * ES;
+#pragma unroll
+    for (int s = 0; s < QV; ++s)
+      qf[rb][s] = valid[rb] ? buf_load16(qr, base + 16 * s) : u32x4{0, 0, 0, 0};
+  }
+
+  // ---- running state per row (log2 units); the sink is counted in lane
+  // group 0 only, since d is summed over the two lanes of a row at the end
+  float m_run[2], d_run[2];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const float s = valid[rb] ? sinks[head[rb]] : kNegInf;
+    m_run[rb] = s * kLog2e;
+    d_run[rb] = (g == 0 && s != kNegInf) ? 1.f : 0.f;
+  }
+  f32x16 acc_o[2][2];
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc_o[db][rb][i] = 0.f;
+
+  // ---- K/V staging: global (buffer loads, zero past the sequence) -> regs -> LDS
+  const uint32_t kv_row_bytes = (uint32_t)hkv * kHeadDim * ES;
+  const __amdgpu_buffer_rsrc_t kr =
+      make_rsrc(k + (size_t)k0 * kv_row_bytes, (uint32_t)((size_t)Lkv * kv_row_bytes));
+  const __amdgpu_buffer_rsrc_t vr =
+      make_rsrc(v + (size_t)k0 * kv_row_bytes, (uint32_t)((size_t)Lkv * kv_row_bytes));
+  constexpr int CPR = kHeadDim * ES / 16;      // 16-byte chunks per key row
+  constexpr int NCH = BK * CPR / 256;          // chunks per thread per tile (K, and V)
+  u32x4 stk[NCH], stv[NCH];
+
+  auto stage_load = [&](int jt) {
+    const int key0 = jt * BK;
+    if constexpr (DT == DT_BF16) {
+#pragma unroll
+      for (int u = 0; u < NCH; ++u) {  // K: chunk c -> key c / 8, part c % 8
+        const int c = tid + 256 * u, key = c / CPR, part = c % CPR;
+        stk[u] = buf_load16(kr, (uint32_t)(key0 + key) * kv_row_bytes + kvh * kHeadDim * ES + part * 16);
+      }
+      // V: thread -> key pair kp = tid / 8, part tid % 8; keys 2kp and 2kp+1
+      const int kp = tid / CPR, part = tid % CPR;
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        stv[u] = buf_load16(vr, (uint32_t)(key0 + 2 * kp + u) * kv_row_bytes + kvh * kHeadDim * ES + part * 16);
+    } else {
+#pragma unroll
+      for (int u = 0; u < NCH; ++u) {
+        const int c = tid + 256 * u, key = c / CPR, part = c % CPR;
+        stk[u] = buf_load16(kr, (uint32_t)(key0 + key) * kv_row_bytes + kvh * kHeadDim * ES + part * 16);
+        stv[u] = buf_load16(vr, (uint32_t)(key0 + key) * kv_row_bytes + kvh * kHeadDim * ES + part * 16);
+      }
+    }
+  };
+
+  auto stage_store = [&](int buf) {
+    char* kd = lds_k[buf];
+    char* vd = lds_v[buf];
+    if constexpr (DT == DT_BF16) {
+#pragma unroll
+      for (int u = 0; u < NCH; ++u) {
+        const int c = tid + 256 * u, key = c / CPR, part = c % CPR;
+        *reinterpret_cast<u32x4*>(kd + (key * KROW + part * 8) * ES) = stk[u];
+      }
+      const int kp = tid / CPR, part = tid % CPR;
+      // Vt[dim][key]: word (V[2kp][dim], V[2kp+1][dim]) for dims 8*part + i
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const unsigned int a = stv[0][i >> 1], bb = stv[1][i >> 1];
+        const unsigned int word = (i & 1) ? ((a >> 16) | (bb & 0xffff0000u))
+                                          : ((a & 0xffffu) | (bb << 16));
+        *reinterpret_cast<unsigned int*>(vd + ((8 * part + i) * VROW + 2 * kp) * ES) = word;
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < NCH; ++u) {
+        const int c = tid + 256 * u, key = c / CPR, part = c % CPR;
+        *reinterpret_cast<u32x4*>(kd + (key * KROW + part * 4) * ES) = stk[u];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          *reinterpret_cast<unsigned int*>(vd + ((4 * part + i) * VROW + key) * ES) = stv[u][i];
+      }
+    }
+  };
+
+  auto compute_tile = [&](int buf, int jt) {
+    const char* kd = lds_k[buf];
+    const char* vd = lds_v[buf];
+    f32x16 sacc[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[kb][rb][i] = 0.f;
+
+    // S^T = K Q^T
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const char* krow = kd + ((kb * 32 + col) * KROW + 32 * g) * ES;
+#pragma unroll
+      for (int s = 0; s < QV; ++s) {
+        const u32x4 kf = *reinterpret_cast<const u32x4*>(krow + 16 * s);
+        if constexpr (DT == DT_BF16) {
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb)
+            sacc[kb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, kf), __builtin_bit_cast(bf16x8, qf[rb][s]),
+                sacc[kb][rb], 0, 0, 0);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+              sacc[kb][rb] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                  __uint_as_float(kf[e]), __uint_as_float(qf[rb][s][e]), sacc[kb][rb], 0, 0, 0);
+        }
+      }
+    }
+
+    // online softmax per row block
+    const bool need_mask = (jt * BK + BK - 1) > lim_min;
+    u32x4 pf[2][2][2];  // bf16 P^T operands [rb][kb][half]
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = jt * BK + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+            if (key > lim[rb]) sacc[kb][rb][r] = kNegInf;
+          }
+      }
+      float mx = kNegInf;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][rb][r]);
+      mx = xor_max(mx, 32);
+      const float m_new = fmaxf(m_run[rb], mx * qk_scale_log2);
+      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run[rb] - m_use);
+      float psum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float pr = fast_exp2(__builtin_fmaf(sacc[kb][rb][r], qk_scale_log2, -m_use));
+          sacc[kb][rb][r] = pr;
+          psum += pr;
+        }
+      d_run[rb] = d_run[rb] * alpha + psum;
+      m_run[rb] = m_new;
+#pragma unroll
+      for (int db = 0; db < 2; ++db) acc_o[db][rb] *= alpha;
+      if constexpr (DT == DT_BF16) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              pf[rb][kb][hh][e] = pack_bf16x2(sacc[kb][rb][8 * hh + 2 * e], sacc[kb][rb][8 * hh + 2 * e + 1]);
+      }
+    }
+
+    // O^T += V^T P^T
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+      const char* vrow = vd + ((db * 32 + col) * VROW) * ES;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        if constexpr (DT == DT_BF16) {
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int key = kb * 32 + 16 * hh + 4 * g;
+            const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + key * ES);
+            const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + (key + 8) * ES);
+            const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+              acc_o[db][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                  __builtin_bit_cast(bf16x8, vf), __builtin_bit_cast(bf16x8, pf[rb][kb][hh]),
+                  acc_o[db][rb], 0, 0, 0);
+          }
+        } else {
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd) {
+            const u32x4 vf =
+                *reinterpret_cast<const u32x4*>(vrow + (kb * 32 + 8 * qd + 4 * g) * ES);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+              for (int rb = 0; rb < 2; ++rb)
+                acc_o[db][rb] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                    __uint_as_float(vf[e]), sacc[kb][rb][4 * qd + e], acc_o[db][rb], 0, 0, 0);
+          }
+        }
+      }
+    }
+  };
+
+  if (n_tiles > 0) {
+    stage_load(0);
+    stage_store(0);
+    __syncthreads();
+    for (int jt = 0; jt < n_tiles; ++jt) {
+      const bool more = jt + 1 < n_tiles;
+      if (more) stage_load(jt + 1);
+      compute_tile(jt & 1, jt);
+      if (more) stage_store((jt + 1) & 1);
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue: out = O / d, rows of this lane, dims 32db + 8qd + 4g + 0..3
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const float dsum = xor_sum(d_run[rb], 32);
+    if (!valid[rb]) continue;
+    const float inv = dsum > 0.f ? 1.f / dsum : 0.f;
+    char* orow = out + (((size_t)q0 + tok[rb]) * hq + head[rb]) * kHeadDim * ES;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        const int d0 = 32 * db + 8 * qd + 4 * g;
+        const float y0 = acc_o[db][rb][4 * qd + 0] * inv, y1 = acc_o[db][rb][4 * qd + 1] * inv;
+        const float y2 = acc_o[db][rb][4 * qd + 2] * inv, y3 = acc_o[db][rb][4 * qd + 3] * inv;
+        if constexpr (DT == DT_BF16) {
+          *reinterpret_cast<u32x2*>(orow + d0 * ES) = u32x2{pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
+        } else {
+          *reinterpret_cast<f32x4*>(orow + d0 * ES) = f32x4{y0, y1, y2, y3};
+        }
+      }
+  }
+}
+
+// ============================================================= host side
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool finite_positive(float x) { return x > 0.f && x < __builtin_huge_valf(); }
+
+int launch_status() {
+  return hipGetLastError() == hipSuccess ? ATTN_SINK_OK : ATTN_SINK_ERR_LAUNCH;
+}
+
+constexpr int kDecodeWaves = 4;
+constexpr int kDecodeUnroll = 4;
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_sink_status_string(int status) {
+  switch (status) {
+    case ATTN_SINK_OK: return "ok";
+    case ATTN_SINK_ERR_INVALID_ARG: return "invalid argument";
+    case ATTN_SINK_ERR_UNSUPPORTED: return "unsupported configuration";
+    case ATTN_SINK_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int attn_sink_prefill(const void* q, const void* k, const void* v, const float* sinks,
+                      const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv, int batch,
+                      int total_q, int total_kv, int max_seqlen_q, int num_kv_heads,
+                      int group_size, int head_dim, float sm_scale, int causal, int dtype,
+                      void* out, void* stream) {
+  // q/out may be NULL only for an empty query set, k/v only for an empty key set
+  if (!sinks || !cu_seqlens_q || !cu_seqlens_kv || ((!q || !out) && total_q != 0) ||
+      ((!k || !v) && total_kv != 0))
+    return ATTN_SINK_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+      !aligned(sinks, 4) || !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_kv, 4))
+    return ATTN_SINK_ERR_INVALID_ARG;
+  if (batch < 0 || total_q < 0 || total_kv < 0 || max_seqlen_q < 0 || num_kv_heads < 1 ||
+      group_size < 1 || head_dim < 1 || (causal != 0 && causal != 1) ||
+      (dtype != ATTN_SINK_F32 && dtype != ATTN_SINK_BF16) || !finite_positive(sm_scale))
+    return ATTN_SINK_ERR_INVALID_ARG;
+  if (head_dim != kHeadDim || group_size > 64) return ATTN_SINK_ERR_UNSUPPORTED;
+  if (batch > 65535 || num_kv_heads > 65535) return ATTN_SINK_ERR_UNSUPPORTED;
+  const int es = dtype == ATTN_SINK_BF16 ? 2 : 4;
+  const int64_t hq = (int64_t)num_kv_heads * group_size;
+  // buffer offsets are 32-bit: each whole tensor must stay below 4 GiB
+  if ((int64_t)total_q * hq * kHeadDim * es >= (int64_t)1 << 32 ||
+      (int64_t)total_kv * num_kv_heads * kHeadDim * es >= (int64_t)1 << 32)
+    return ATTN_SINK_ERR_UNSUPPORTED;
+  if (batch == 0 || total_q == 0 || max_seqlen_q == 0) return ATTN_SINK_OK;
+  const int tb = 4 * (64 / group_size);
+  const int n_qtiles = (max_seqlen_q + tb - 1) / tb;
+  const dim3 grid(n_qtiles, num_kv_heads, batch);
+  const float qk = sm_scale * kLog2e;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (dtype == ATTN_SINK_BF16)
+    hipLaunchKernelGGL(prefill_kernel<DT_BF16>, grid, dim3(256), 0, s, (const char*)q,
+                       (const char*)k, (const char*)v, sinks, cu_seqlens_q, cu_seqlens_kv,
+                       total_q, total_kv, num_kv_heads, group_size, qk, causal, n_qtiles,
+                       (char*)out);
+  else
+    hipLaunchKernelGGL(prefill_kernel<DT_F32>, grid, dim3(256), 0, s, (const char*)q,
+                       (const char*)k, (const char*)v, sinks, cu_seqlens_q, cu_seqlens_kv,
+                       total_q, total_kv, num_kv_heads, group_size, qk, causal, n_qtiles,
+                       (char*)out);
+  return launch_status();
+}
+
+int attn_sink_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* page_table, const int32_t* kv_lens, const float* sinks,
+                           int batch, int max_pages_per_seq, int num_pages, int num_kv_heads,
+                           int group_size, int head_dim, int page_size, float sm_scale,
+                           int dtype, int num_splits, float* partial_m, float* partial_d,
+                           float* partial_o, void* out, void* stream) {
+  // the caches may be NULL only when they hold no page
+  if (!q || !page_table || !kv_lens || !sinks || ((!k_cache || !v_cache) && num_pages != 0))
+    return ATTN_SINK_ERR_INVALID_ARG;
+  if (num_splits < 1) return ATTN_SINK_ERR_INVALID_ARG;
+  if (num_splits == 1 && !out) return ATTN_SINK_ERR_INVALID_ARG;
+  if (num_splits > 1 && (!partial_m || !partial_d || !partial_o)) return ATTN_SINK_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(page_table, 4) || !aligned(kv_lens, 4) || !aligned(sinks, 4) ||
+      (out && !aligned(out, 16)) || (partial_m && !aligned(partial_m, 4)) ||
+      (partial_d && !aligned(partial_d, 4)) || (partial_o && !aligned(partial_o, 16)))
+    return ATTN_SINK_ERR_INVALID_ARG;
+  if (batch < 0 || max_pages_per_seq < 1 || num_pages < 0 || num_kv_heads < 1 ||
+      group_size < 1 || head_dim < 1 || page_size < 1 ||
+      (dtype != ATTN_SINK_F32 && dtype != ATTN_SINK_BF16) || !finite_positive(sm_scale))
+    return ATTN_SINK_ERR_INVALID_ARG;
+  if (head_dim != kHeadDim || page_size != kPage || group_size > 16)
+    return ATTN_SINK_ERR_UNSUPPORTED;
+  if (batch > 65535 || num_kv_heads > 65535 ||
+      (int64_t)max_pages_per_seq * kPage > INT32_MAX ||
+      (int64_t)num_splits * max_pages_per_seq > INT32_MAX)
+    return ATTN_SINK_ERR_UNSUPPORTED;
+  if (batch == 0) return ATTN_SINK_OK;
+  const dim3 grid(num_splits, num_kv_heads, batch);
+  const float qk = sm_scale * kLog2e;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (dtype == ATTN_SINK_BF16)
+    hipLaunchKernelGGL((decode_kernel<DT_BF16, kDecodeWaves, kDecodeUnroll>), grid,
+                       dim3(64 * kDecodeWaves), 0, s, (const char*)q, (const char*)k_cache,
+                       (const char*)v_cache, page_table, kv_lens, sinks, max_pages_per_seq,
+                       num_pages, num_kv_heads, group_size, qk, num_splits, partial_m,
+                       partial_d, partial_o, (char*)out);
+  else
+    hipLaunchKernelGGL((decode_kernel<DT_F32, kDecodeWaves, kDecodeUnroll>), grid,
+                       dim3(64 * kDecodeWaves), 0, s, (const char*)q, (const char*)k_cache,
+                       (const char*)v_cache, page_table, kv_lens, sinks, max_pages_per_seq,
+                       num_pages, num_kv_heads, group_size, qk, num_splits, partial_m,
+                       partial_d, partial_o, (char*)out);
+  return launch_status();
+}
+
+int attn_sink_merge(const float* partial_m, const float* partial_d, const float* partial_o,
+                    int batch, int num_q_heads, int num_splits, int head_dim, int out_dtype,
+                    void* out, void* stream) {
+  if (!partial_m || !partial_d || !partial_o || !out) return ATTN_SINK_ERR_INVALID_ARG;
+  if (!aligned(partial_m, 4) || !aligned(partial_d, 4) || !aligned(partial_o, 16) ||
+      !aligned(out, 16))
+    return ATTN_SINK_ERR_INVALID_ARG;
+  if (batch < 0 || num_q_heads < 1 || num_splits < 1 || head_dim < 1 ||
+      (out_dtype != ATTN_SINK_F32 && out_dtype != ATTN_SINK_BF16))
+    return ATTN_SINK_ERR_INVALID_ARG;
+  if (head_dim != kHeadDim) return ATTN_SINK_ERR_UNSUPPORTED;
+  const int64_t rows = (int64_t)batch * num_q_heads;
+  if (rows > INT32_MAX - 3) return ATTN_SINK_ERR_UNSUPPORTED;
+  if (rows == 0) return ATTN_SINK_OK;
+  const dim3 grid((unsigned)((rows + 3) / 4));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (out_dtype == ATTN_SINK_BF16)
+    hipLaunchKernelGGL(merge_kernel<DT_BF16>, grid, dim3(256), 0, s, partial_m, partial_d,
+                       partial_o, (int)rows, num_splits, (char*)out);
+  else
+    hipLaunchKernelGGL(merge_kernel<DT_F32>, grid, dim3(256), 0, s, partial_m, partial_d,
+                       partial_o, (int)rows, num_splits, (char*)out);
+  return launch_status();
+}
+
+}  // extern "C"

@@ -1,0 +1,147 @@
+/*
+ * attn_sink.h -- C ABI of the MI355X (gfx950) grouped-query attention library
+ * with per-head attention sinks.
+ *
+ * The operation.  Page "GPT-OSS on Day 0" (perplexity.ai), section
+ * "Attention: GQA with Attention Sinks": grouped-query attention in which
+ * every query head owns one pre-trained sink value that takes part in the
+ * softmax.  Section "Kernels for GPT-OSS / Sink Attention" of the same page:
+ * the sink is an extra term before the softmax next to the Q.K^T products; the
+ * softmax runs online with a running max m and scale d; m starts from the
+ * head's sink instead of -inf; the work is spread over heads and over blocks
+ * of the key length, and only the first block of a split carries the sink.
+ * For one query row with visible keys j < n:
+ *
+ *     x_j = sm_scale * (q . k_j)
+ *     w   = softmax([x_0 .. x_{n-1}, s_h])     (the sink is one more logit)
+ *     out = sum_{j<n} w_j v_j                  (the sink has no value row)
+ *
+ * The sink is in the same natural-log units as x_j and is NOT multiplied by
+ * sm_scale; s_h = -inf turns it off.  Query head h reads key/value head
+ * h / group_size.  Page "Fast embeddings on GPUs", section "ROSE": ragged
+ * (unpadded, packed) batches for prefill and a paged key/value cache for
+ * decode.
+ *
+ * Conventions shared by every entry point:
+ *   - every pointer argument is a DEVICE pointer except where stated; the
+ *     caller owns every buffer and keeps it alive until the stream's work is
+ *     done; the library allocates nothing and keeps no state;
+ *   - calls only enqueue work on `stream` (a hipStream_t passed as void*;
+ *     NULL = the null stream): no host synchronisation and no device-to-host
+ *     copy, so the calls can be captured into a HIP graph;
+ *   - the returned status is host-side: argument errors are detected before
+ *     anything is enqueued; ATTN_SINK_ERR_LAUNCH reports a failed launch;
+ *   - element type `dtype`: ATTN_SINK_F32 or ATTN_SINK_BF16 for q, k, v and
+ *     out; sinks and split partials are always fp32;
+ *   - head_dim must be 64 and page_size 16 (ATTN_SINK_ERR_UNSUPPORTED
+ *     otherwise); every tensor pointer must be 16-byte aligned;
+ *   - device-side integer contents (cumulative offsets, lengths, page ids)
+ *     are clamped, never trusted: offsets are clamped to [0, total], lengths
+ *     to [0, capacity], and a page id outside [0, num_pages) makes its page
+ *     skipped, so bad contents give wrong numbers, never a memory fault.
+ */
+#ifndef ATTN_SINK_H
+#define ATTN_SINK_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ATTN_SINK_OK = 0,
+    ATTN_SINK_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size or flag */
+    ATTN_SINK_ERR_UNSUPPORTED = 2, /* valid but not built: head_dim, page size, group */
+    ATTN_SINK_ERR_LAUNCH = 3       /* the HIP runtime refused the launch */
+} attn_sink_status;
+
+typedef enum { ATTN_SINK_F32 = 0, ATTN_SINK_BF16 = 1 } attn_sink_dtype;
+
+/*
+ * Ragged prefill (causal or not) with sinks.
+ * Passage: "GPT-OSS on Day 0", sections "Attention: GQA with Attention
+ * Sinks" and "Kernels for GPT-OSS / Sink Attention"; ragged layout from
+ * "Fast embeddings on GPUs", section "ROSE".
+ *
+ *   q     [total_q,  Hkv*G, D] dtype, token-major (sequences packed)
+ *   k, v  [total_kv, Hkv,   D] dtype
+ *   sinks [Hkv*G] fp32, natural-log units; -inf allowed, +inf is not
+ *   cu_seqlens_q, cu_seqlens_kv [batch+1] int32 prefix offsets
+ *         (cu[0] = 0, non-decreasing, cu[batch] = total)
+ *   max_seqlen_q: host-side upper bound on any sequence's query count; it
+ *         sizes the grid, and query rows beyond it are not written
+ *   group_size G in 1..64; num_kv_heads >= 1; head_dim = 64
+ *   sm_scale > 0 and finite; causal in {0, 1}: causal masks are aligned to
+ *         the bottom-right corner (row i sees keys j <= i + Lkv - Lq)
+ *   out   [total_q, Hkv*G, D] dtype; a row with no visible key gets 0
+ * q and out may be NULL when total_q == 0, k and v when total_kv == 0.
+ * Each of q, k, v must be below 4 GiB (ATTN_SINK_ERR_UNSUPPORTED otherwise).
+ */
+int attn_sink_prefill(const void *q, const void *k, const void *v,
+                      const float *sinks, const int32_t *cu_seqlens_q,
+                      const int32_t *cu_seqlens_kv, int batch, int total_q,
+                      int total_kv, int max_seqlen_q, int num_kv_heads,
+                      int group_size, int head_dim, float sm_scale, int causal,
+                      int dtype, void *out, void *stream);
+
+/*
+ * Paged decode (one query token per sequence) with sinks, optionally split
+ * along the key length.
+ * Passage: "GPT-OSS on Day 0", section "Kernels for GPT-OSS / Sink
+ * Attention" (split over key blocks, sink in the first block only); paged
+ * cache from "Fast embeddings on GPUs", section "ROSE".
+ *
+ *   q          [batch, Hkv*G, D] dtype
+ *   k_cache    [num_pages, Hkv, page_size, D] dtype (token-major pages)
+ *   v_cache    [num_pages, Hkv, D, page_size] dtype (dim-major pages)
+ *   page_table [batch, max_pages_per_seq] int32: physical page of each
+ *              logical page; entries past ceil(kv_len/page_size) are unread
+ *   kv_lens    [batch] int32, clamped to [0, max_pages_per_seq*page_size]
+ *   sinks      [Hkv*G] fp32
+ *   group_size G in 1..16; page_size = 16; head_dim = 64
+ *   num_splits S >= 1: sequence b's np = ceil(kv_len/16) pages are cut into
+ *              chunks of ppc = ceil(np/S) pages; chunk c covers tokens
+ *              [c*ppc*16, min((c+1)*ppc*16, kv_len)).  Chunk 0 carries the
+ *              sink; an empty chunk c > 0 yields (m, d, o) = (-inf, 0, 0).
+ *   S == 1:    writes out [batch, Hkv*G, D] dtype; partials may be NULL.
+ *   k_cache and v_cache may be NULL when num_pages == 0.
+ *   S  > 1:    writes partial_m, partial_d [batch, Hkv*G, S] and
+ *              partial_o [batch, Hkv*G, S, D] (fp32; m in natural-log
+ *              units, o unnormalised relative to m); out is not touched and
+ *              may be NULL -- attn_sink_merge finishes the job.
+ */
+int attn_sink_decode_paged(const void *q, const void *k_cache,
+                           const void *v_cache, const int32_t *page_table,
+                           const int32_t *kv_lens, const float *sinks,
+                           int batch, int max_pages_per_seq, int num_pages,
+                           int num_kv_heads, int group_size, int head_dim,
+                           int page_size, float sm_scale, int dtype,
+                           int num_splits, float *partial_m, float *partial_d,
+                           float *partial_o, void *out, void *stream);
+
+/*
+ * Merge of split-KV partial states into the final output; the sink is
+ * already inside chunk 0's state, so it is counted exactly once.
+ * Passage: "GPT-OSS on Day 0", section "Kernels for GPT-OSS / Sink
+ * Attention" (blocks along the key length, sink only in the first).
+ *
+ *   partial_m, partial_d [batch, num_q_heads, num_splits] fp32
+ *   partial_o            [batch, num_q_heads, num_splits, head_dim] fp32
+ *   out [batch, num_q_heads, head_dim], out_dtype (F32 or BF16, RNE)
+ *   out = (sum_c o_c e^(m_c - M)) / (sum_c d_c e^(m_c - M)), M = max_c m_c;
+ *   a row whose m_c are all -inf gets 0.
+ */
+int attn_sink_merge(const float *partial_m, const float *partial_d,
+                    const float *partial_o, int batch, int num_q_heads,
+                    int num_splits, int head_dim, int out_dtype, void *out,
+                    void *stream);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char *attn_sink_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_SINK_H */

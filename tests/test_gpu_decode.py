@@ -1,0 +1,241 @@
+"""GPU parity of paged decode, split-KV partials and the merge (MI355X).
+
+Every comparison is against the fp64 oracle on the same (rounded) inputs, or
+is a bit-exact construction whose answer is known without arithmetic.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from helpers import assert_close, tol_for
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _to_dev(d):
+    return {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+
+
+def run_decode(lib, d, splits):
+    """Decode through the C ABI; splits > 1 goes through attn_sink_merge."""
+    q = d["q"]
+    if splits == 1:
+        out = lib.attn_sink_decode_paged(q, d["k_cache"], d["v_cache"], d["page_table"],
+                                         d["kv_lens"], d["sinks"], d["group"],
+                                         d["sm_scale"], 1)
+        return out, None
+    pm, pd, po = lib.attn_sink_decode_paged(q, d["k_cache"], d["v_cache"], d["page_table"],
+                                            d["kv_lens"], d["sinks"], d["group"],
+                                            d["sm_scale"], splits)
+    out = lib.attn_sink_merge(pm, pd, po, out_dtype=q.dtype)
+    return out, (pm, pd, po)
+
+
+def oracle_decode(d, rows=None):
+    return oracle.decode_paged(d["q"].cpu(), d["k_cache"].cpu(), d["v_cache"].cpu(),
+                               d["page_table"].cpu(), d["kv_lens"].cpu(), d["sinks"].cpu(),
+                               d["group"], d["sm_scale"], rows=rows)
+
+
+LENS = [0, 1, 15, 16, 17, 31, 100, 4097]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("group", [1, 4, 8, 16])
+@pytest.mark.parametrize("splits", [1, 2, 7, 64, 300])
+def test_decode_sweep_matches_oracle(lib, dtype, group, splits):
+    d = workloads.decode_inputs(LENS, hq=2 * group, hkv=2, dtype=dtype, seed=group * 100 + splits,
+                                sink_std=1.5, extra_pages=3)
+    dd = _to_dev(d)
+    out, _ = run_decode(lib, dd, splits)
+    torch.cuda.synchronize()
+    ref = oracle_decode(d)
+    assert_close(out, ref, dtype, "decode G=%d S=%d %s" % (group, splits, dtype))
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_partials_match_oracle_and_bookkeeping(lib, dtype):
+    """Chunk states: the empty/non-empty pattern and chunk 0's sink-only state
+    are exact; finite m, d and o/d match the oracle's partials."""
+    lens, S = [0, 5, 16, 40, 200, 1000], 6
+    d = workloads.decode_inputs(lens, hq=8, hkv=2, dtype=dtype, seed=31, sink_std=1.5)
+    dd = _to_dev(d)
+    _, (pm, pd, po) = run_decode(lib, dd, S)
+    torch.cuda.synchronize()
+    rm, rd, ro = oracle.decode_partials(d["q"], d["k_cache"], d["v_cache"], d["page_table"],
+                                        d["kv_lens"], d["sinks"], d["group"], d["sm_scale"], S)
+    gm, gd, go = pm.cpu().double().numpy(), pd.cpu().double().numpy(), po.cpu().double().numpy()
+    empty = rm == -math.inf
+    np.testing.assert_array_equal(gm == -math.inf, empty)
+    np.testing.assert_array_equal(gd[empty], 0.0)
+    np.testing.assert_array_equal(go[empty], 0.0)
+    # zero-length sequence: chunk 0 is exactly the sink state (s, 1, 0)
+    np.testing.assert_array_equal(gd[0, :, 0], 1.0)
+    np.testing.assert_array_equal(go[0, :, 0], 0.0)
+    np.testing.assert_allclose(gm[0, :, 0], d["sinks"].double().numpy(), rtol=1e-6)
+    live = ~empty
+    np.testing.assert_allclose(gm[live], rm[live], rtol=1e-5, atol=1e-5)
+    np.testing.assert_allclose(gd[live], rd[live], rtol=1e-3 if dtype == torch.bfloat16 else 1e-5)
+    atol, rtol = tol_for(dtype)
+    on = go[live] / gd[live][:, None]
+    rn = ro[live] / rd[live][:, None]
+    assert np.all(np.abs(on - rn) <= atol + rtol * np.abs(rn))
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_merge_one_hot_is_bit_exact(lib, out_dtype):
+    """Exactly one chunk per row has a finite m (others (-inf, 0, 0)) and
+    d = 2^k: the merged output must be o / 2^k exactly (then RNE to bf16)."""
+    B, H, S, D = 3, 8, 11, 64
+    g = torch.Generator().manual_seed(5)
+    m = torch.full((B, H, S), -math.inf)
+    dd = torch.zeros(B, H, S)
+    o = torch.zeros(B, H, S, D)
+    pick = torch.randint(0, S, (B, H), generator=g)
+    kexp = torch.randint(-3, 6, (B, H), generator=g)
+    ohot = torch.randn(B, H, D, generator=g)
+    for b in range(B):
+        for h in range(H):
+            c = int(pick[b, h])
+            m[b, h, c] = float(torch.randn(1, generator=g)) * 5
+            dd[b, h, c] = 2.0 ** int(kexp[b, h])
+            o[b, h, c] = ohot[b, h]
+    out = lib.attn_sink_merge(m.to(DEV), dd.to(DEV), o.to(DEV), out_dtype=out_dtype)
+    expect = ohot / (2.0 ** kexp.float()).unsqueeze(-1)
+    torch.testing.assert_close(out.cpu(), expect.to(out_dtype), rtol=0, atol=0)
+
+
+def test_merge_all_empty_rows_give_zero(lib):
+    m = torch.full((2, 4, 3), -math.inf, device=DEV)
+    z = torch.zeros((2, 4, 3), device=DEV)
+    o = torch.zeros((2, 4, 3, 64), device=DEV)
+    out = lib.attn_sink_merge(m, z, o, out_dtype=torch.float32)
+    assert torch.all(out == 0)
+
+
+def _logical_to_paged(k, v, page, perm_seed, extra=5, fill=float("nan")):
+    """Scatter contiguous per-sequence k/v [L, Hkv, D] lists into one paged
+    cache with a random physical placement."""
+    lens = [x.shape[0] for x in k]
+    hkv, dim = k[0].shape[1], k[0].shape[2]
+    npg = [(L + page - 1) // page for L in lens]
+    total = sum(npg) + extra
+    perm = torch.randperm(total, generator=torch.Generator().manual_seed(perm_seed))
+    kc = torch.full((total, hkv, page, dim), fill, dtype=k[0].dtype)
+    vc = torch.full((total, hkv, dim, page), fill, dtype=v[0].dtype)
+    pt = torch.full((len(lens), max(1, max(npg))), -1, dtype=torch.int32)
+    off = 0
+    for b, L in enumerate(lens):
+        for p in range(npg[b]):
+            phys = int(perm[off + p])
+            pt[b, p] = phys
+            t0, t1 = p * page, min(L, (p + 1) * page)
+            kc[phys, :, :t1 - t0, :] = k[b][t0:t1].permute(1, 0, 2)
+            vc[phys, :, :, :t1 - t0] = v[b][t0:t1].permute(1, 2, 0)
+        off += npg[b]
+    return kc, vc, pt
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("splits", [1, 4])
+def test_page_permutation_invariance_and_tail_poison(lib, dtype, splits):
+    """Two physical placements of the same logical cache give bitwise equal
+    outputs; NaN in unused page slots and unused pages never leaks in."""
+    lens, hq, hkv = [1, 17, 64, 333], 8, 2
+    g = torch.Generator().manual_seed(8)
+    ks = [torch.randn(L, hkv, 64, generator=g).to(dtype) for L in lens]
+    vs = [torch.randn(L, hkv, 64, generator=g).to(dtype) for L in lens]
+    q = torch.randn(len(lens), hq, 64, generator=g).to(dtype)
+    sinks = torch.randn(hq, generator=g)
+    outs = []
+    for seed, fill in ((1, float("nan")), (2, 0.0)):
+        kc, vc, pt = _logical_to_paged(ks, vs, 16, seed, fill=fill)
+        d = dict(q=q, k_cache=kc, v_cache=vc, page_table=pt,
+                 kv_lens=torch.tensor(lens, dtype=torch.int32), sinks=sinks, group=hq // hkv,
+                 sm_scale=0.125)
+        out, _ = run_decode(lib, _to_dev(d), splits)
+        outs.append(out.cpu())
+    assert torch.all(torch.isfinite(outs[0].float()))
+    assert torch.equal(outs[0], outs[1])
+    ref = oracle_decode(dict(q=q, k_cache=kc, v_cache=vc, page_table=pt,
+                             kv_lens=torch.tensor(lens, dtype=torch.int32), sinks=sinks,
+                             group=hq // hkv, sm_scale=0.125))
+    assert_close(outs[1], ref, dtype, "permuted pages")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("splits", [1, 3, 64])
+def test_one_hot_retrieval_is_bit_exact(lib, dtype, splits):
+    """sink = -inf and one key per sequence whose logit is > 1000 above every
+    other: all other weights underflow to exactly 0, d = 1 and the output is
+    that key's value row bit for bit, whichever page and chunk holds it."""
+    lens, hq, hkv = [5, 16, 17, 700, 1601], 8, 2
+    g = torch.Generator().manual_seed(12)
+    targets = [int(torch.randint(0, L, (1,), generator=g)) for L in lens]
+    ks, vs = [], []
+    for L, t in zip(lens, targets):
+        k = torch.rand(L, hkv, 64, generator=g) * 2 - 1
+        k[:, :, 0] = torch.rand(L, hkv, generator=g) * 2 - 1
+        k[t, :, 0] = 128.0
+        ks.append(k.to(dtype))
+        vs.append(torch.randn(L, hkv, 64, generator=g).to(dtype))
+    q = torch.zeros(len(lens), hq, 64)
+    q[:, :, 0] = 64.0
+    q = q.to(dtype)
+    kc, vc, pt = _logical_to_paged(ks, vs, 16, 3)
+    d = dict(q=q, k_cache=kc, v_cache=vc, page_table=pt,
+             kv_lens=torch.tensor(lens, dtype=torch.int32),
+             sinks=torch.full((hq,), -math.inf), group=hq // hkv, sm_scale=0.125)
+    out, _ = run_decode(lib, _to_dev(d), splits)
+    out = out.cpu()
+    for b, t in enumerate(targets):
+        for h in range(hq):
+            assert torch.equal(out[b, h], vs[b][t, h // (hq // hkv)]), (b, h)
+
+
+def test_decode_deterministic(lib):
+    d = _to_dev(workloads.decode_inputs([900, 33, 4000], hq=16, hkv=2, seed=3))
+    a, _ = run_decode(lib, d, 5)
+    b, _ = run_decode(lib, d, 5)
+    assert torch.equal(a, b)
+
+
+def test_decode_c3_full_matches_oracle(lib):
+    """Paged decode workload: B=64, kv_len U[512,8192], 64/8 heads, bf16."""
+    d = workloads.workload(3, device="cpu", cache_device=DEV)
+    dd = _to_dev(d)
+    host = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    ref = oracle_decode(host)
+    from gqa_attention_sinks_initialised_amd import default_num_splits
+    for splits in (1, default_num_splits(d["kv_lens"].tolist(), 8)):
+        out, _ = run_decode(lib, dd, splits)
+        torch.cuda.synchronize()
+        assert_close(out, ref, torch.bfloat16, "C3 splits=%d" % splits)
+
+
+def test_decode_c4_sampled_matches_oracle(lib):
+    """Long split-KV decode workload: B=4, kv_len 131072, 64 splits; sampled
+    (sequence, head) rows of the output and of the partial states."""
+    d = workloads.workload(4, device="cpu", cache_device=DEV)
+    dd = _to_dev(d)
+    out, (pm, pd, po) = run_decode(lib, dd, 64)
+    torch.cuda.synchronize()
+    host = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    rng = np.random.default_rng(4)
+    rb = np.repeat(np.arange(4), 6).astype(np.int32)
+    rh = rng.integers(0, 64, size=len(rb)).astype(np.int32)
+    ref = oracle_decode(host, rows=(rb, rh))
+    got = out.cpu()[torch.as_tensor(rb).long(), torch.as_tensor(rh).long()]
+    assert_close(got, ref, torch.bfloat16, "C4 sampled rows")
+    rm, rd, ro = oracle.decode_partials(host["q"], host["k_cache"], host["v_cache"],
+                                        host["page_table"], host["kv_lens"], host["sinks"],
+                                        8, host["sm_scale"], 64, rows=(rb, rh))
+    gm = pm.cpu()[torch.as_tensor(rb).long(), torch.as_tensor(rh).long()].double().numpy()
+    gd = pd.cpu()[torch.as_tensor(rb).long(), torch.as_tensor(rh).long()].double().numpy()
+    np.testing.assert_allclose(gm, rm, rtol=1e-5, atol=1e-5)
+    np.testing.assert_allclose(gd, rd, rtol=1e-2)
