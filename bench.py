@@ -7,7 +7,7 @@ One step = one pass over every stage of the path on its synthetic workload:
 `value` is the prefill throughput in TFLOP/s (algorithmic flops: 4*D per
 causal-visible (query, key) pair) from HIP events around the prefill launch
 on the stream it runs on; the decode stages report achieved HBM GB/s.  The
-256 MB last-level cache is flushed (1 GiB write) before each decode stage,
+256 MB memory-side cache is flushed (a 1 GiB read) before each decode stage,
 outside the kernel events.  The fp64 CPU oracle is timed on a bounded sample
 of the prefill workload as a reported baseline (rank 0, N=1 only).
 
@@ -94,7 +94,9 @@ def main():
     p3, p4 = mk_partials(64, s3), mk_partials(4, s4)
     o3 = torch.empty((64, hq, 64), device=dev, dtype=torch.bfloat16)
     o4 = torch.empty((4, hq, 64), device=dev, dtype=torch.bfloat16)
-    flush = torch.empty(1 << 30, device=dev, dtype=torch.uint8)
+    # Reading (not writing) 1 GiB evicts the 256 MB memory-side cache without
+    # leaving dirty lines whose write-back would land inside the next kernel.
+    flush = torch.ones(1 << 28, device=dev, dtype=torch.float32)
 
     def run_prefill():
         attn.attn_sink_prefill(c2["q"], c2["k"], c2["v"], c2["sinks"], c2["cu_seqlens_q"],
@@ -116,11 +118,11 @@ def main():
         if evs: e["t0"].record()
         run_prefill()
         if evs: e["t1"].record()
-        flush.fill_(1)
+        flush.sum()
         if evs: e["t2"].record()
         run_decode(c3, s3, p3, o3, e.get("t3"))
         if evs: e["t4"].record()
-        flush.fill_(2)
+        flush.sum()
         if evs: e["t5"].record()
         run_decode(c4, s4, p4, o4, e.get("t6"))
         if evs: e["t7"].record()

@@ -47,6 +47,9 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr int kHeadDim = 64;
 constexpr int kPage = 16;
+// Prefill keeps a stale reference max until a row's max grows by more than
+// this many log2 units, so probabilities stay below 2^8 between rescales.
+constexpr float kRescaleLog2 = 8.0f;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -54,6 +57,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 enum { DT_F32 = ATTN_SINK_F32, DT_BF16 = ATTN_SINK_BF16 };
 
@@ -74,9 +79,19 @@ __device__ __forceinline__ unsigned short to_bf16(float x) {
   return __builtin_bit_cast(unsigned short, static_cast<__bf16>(x));
 }
 
+// Two fp32 -> packed bf16 pair (lo in bits 0..15), one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ unsigned int pack_bf16x2(float lo, float hi) {
-  return (unsigned int)to_bf16(lo) | ((unsigned int)to_bf16(hi) << 16);
+  return __builtin_bit_cast(unsigned int, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
+
+// acc + lo + hi of a packed bf16 pair (v_dot2_f32_bf16 against (1, 1)).
+__device__ __forceinline__ float add_bf16x2(unsigned int pk, float acc) {
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones, acc, false);
+}
+
+// True on every lane if the predicate holds on any lane of the wave.
+__device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 
 __device__ __forceinline__ float bf16_lo(unsigned int w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(unsigned int w) { return __uint_as_float(w & 0xffff0000u); }
@@ -263,27 +278,46 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(
     }
   };
 
-  // Page walk: this wave takes pages p_begin + w, + WAVES, ...; UNROLL pages
-  // are loaded before any is consumed so several loads are in flight.
-  int p = p_begin + w;
-  for (; p + (UNROLL - 1) * WAVES < p_end; p += UNROLL * WAVES) {
-    DecodeFrag<DT> f[UNROLL];
-    int phys[UNROLL];
+  // Page walk.  This wave takes pages p_begin + w + WAVES*k, k = 0 .. n_mine-1.
+  // Their physical ids are fetched once per 64 pages into one VGPR (lane k
+  // holds page k's id) and read back with v_readlane, so the loop never waits
+  // on a scalar load.  Page data is double-buffered in registers: the loads
+  // of the next UNROLL pages are issued before the current UNROLL pages are
+  // consumed, keeping 2*UNROLL pages of this wave in flight.
+  const int n_mine = p_end - p_begin - w > 0 ? (p_end - p_begin - w + WAVES - 1) / WAVES : 0;
+  int ids = -1;
+  auto fetch_ids = [&](int k0) {
+    const int k = k0 + lane;
+    ids = (k < n_mine) ? pt[p_begin + w + k * WAVES] : -1;
+  };
+  auto phys_of = [&](int k) { return __builtin_amdgcn_readlane(ids, k & 63); };
+  auto load_group = [&](int k0, DecodeFrag<DT>* f, int* ph) {
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
-      phys[u] = __builtin_amdgcn_readfirstlane(pt[p + u * WAVES]);
-      if ((unsigned)phys[u] < (unsigned)num_pages) load_page(phys[u], f[u]);
+      ph[u] = (k0 + u < n_mine) ? phys_of(k0 + u) : -1;
+      if ((unsigned)ph[u] < (unsigned)num_pages) load_page(ph[u], f[u]);
     }
+  };
+  auto compute_group = [&](int k0, DecodeFrag<DT>* f, const int* ph) {
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u)
-      if ((unsigned)phys[u] < (unsigned)num_pages) compute_page(f[u], p + u * WAVES);
-  }
-  for (; p < p_end; p += WAVES) {
-    DecodeFrag<DT> f;
-    const int phys = __builtin_amdgcn_readfirstlane(pt[p]);
-    if ((unsigned)phys < (unsigned)num_pages) {
-      load_page(phys, f);
-      compute_page(f, p);
+      if ((unsigned)ph[u] < (unsigned)num_pages) compute_page(f[u], p_begin + w + (k0 + u) * WAVES);
+  };
+  static_assert(64 % UNROLL == 0, "page groups must not straddle an id block");
+  if (n_mine > 0) {
+    DecodeFrag<DT> fa[UNROLL], fb[UNROLL];
+    int pa[UNROLL], pb[UNROLL];
+    fetch_ids(0);
+    load_group(0, fa, pa);
+    for (int k = 0; k < n_mine; k += 2 * UNROLL) {
+      // ids for the group after next must be resident before it is loaded
+      if (((k + UNROLL) & 63) == 0 && k + UNROLL < n_mine) fetch_ids(k + UNROLL);
+      if (k + UNROLL < n_mine) load_group(k + UNROLL, fb, pb);
+      compute_group(k, fa, pa);
+      if (k + UNROLL >= n_mine) break;
+      if (((k + 2 * UNROLL) & 63) == 0 && k + 2 * UNROLL < n_mine) fetch_ids(k + 2 * UNROLL);
+      if (k + 2 * UNROLL < n_mine) load_group(k + 2 * UNROLL, fa, pa);
+      compute_group(k + UNROLL, fb, pb);
     }
   }
 
@@ -343,44 +377,74 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(
 
 // ============================================================= merge kernel
 //
-// One wave per (sequence, query head) row; lane = output dim.  Split states
-// are read 64 at a time (lane c holds chunk c's m and d), their weights
-// e^(m_c - M) are formed once per chunk and broadcast across the wave.
+// CL*16 threads per (sequence, query head) row: thread (cl, dq) owns output
+// dims [4dq, 4dq+4) and the chunks c = cl, cl + CL, ...; partial o rows are
+// read with 16-byte loads (a chunk's 64 dims are 256 contiguous bytes).  The
+// chunk weights e^(m_c - M) and D = sum d_c e^(m_c - M) are formed by the
+// row's first wave; the CL partial sums of o are combined through LDS.
 
-template <int DT>
+template <int DT, int CL>
 __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pm,
                                                     const float* __restrict__ pd,
                                                     const float* __restrict__ po, int rows,
                                                     int splits, char* __restrict__ out) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
+  constexpr int TPR = 16 * CL;           // threads per row
+  constexpr int RPB = 256 / TPR;         // rows per block
+  __shared__ float sm_M[RPB], sm_D[RPB];
+  __shared__ f32x4 sm_o[RPB][CL][16];
+  const int t = threadIdx.x % TPR, rl = threadIdx.x / TPR;
+  const int row = blockIdx.x * RPB + rl;
+  const int cl = t >> 4, dq = t & 15;
+  const bool live = row < rows;
   const float* m = pm + (size_t)row * splits;
   const float* d = pd + (size_t)row * splits;
-  const float* o = po + (size_t)row * splits * kHeadDim;
-  float M = kNegInf;
-  for (int c = lane; c < splits; c += 64) M = fmaxf(M, m[c]);
-#pragma unroll
-  for (int k = 1; k < 64; k <<= 1) M = xor_max(M, k);
-  float D = 0.f, O = 0.f;
-  for (int c0 = 0; c0 < splits; c0 += 64) {
-    const int c = c0 + lane;
-    const float mc = c < splits ? m[c] : kNegInf;
-    const float wc = (mc == kNegInf) ? 0.f : fast_exp2((mc - M) * kLog2e);
-    D += (c < splits ? d[c] : 0.f) * wc;
-    const int nc = min(64, splits - c0);
-    for (int i = 0; i < nc; ++i) {
-      const float wi = __shfl(wc, i, 64);
-      O += wi * o[(size_t)(c0 + i) * kHeadDim + lane];
+  // M and D by the first (up to 64) threads of the row
+  if (t < 64) {
+    float M = kNegInf, D = 0.f;
+    if (live) {
+      for (int c = t; c < splits; c += 64) M = fmaxf(M, m[c]);
+    }
+    const int lanes = TPR < 64 ? TPR : 64;
+    for (int k = 1; k < lanes; k <<= 1) M = fmaxf(M, __shfl_xor(M, k, lanes));
+    if (live) {
+      for (int c = t; c < splits; c += 64) {
+        const float mc = m[c];
+        D += (mc == kNegInf) ? 0.f : d[c] * fast_exp2((mc - M) * kLog2e);
+      }
+    }
+    for (int k = 1; k < lanes; k <<= 1) D += __shfl_xor(D, k, lanes);
+    if (t == 0) {
+      sm_M[rl] = M;
+      sm_D[rl] = D;
     }
   }
+  __syncthreads();
+  const float M = sm_M[rl];
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (live) {
+    const float* o = po + (size_t)row * splits * kHeadDim + 4 * dq;
+    for (int c = cl; c < splits; c += CL) {
+      const float mc = m[c];
+      if (mc == kNegInf) continue;
+      acc += fast_exp2((mc - M) * kLog2e) * *reinterpret_cast<const f32x4*>(o + (size_t)c * kHeadDim);
+    }
+  }
+  sm_o[rl][cl][dq] = acc;
+  __syncthreads();
+  if (cl == 0 && live) {
+    f32x4 sum = sm_o[rl][0][dq];
 #pragma unroll
-  for (int k = 1; k < 64; k <<= 1) D = xor_sum(D, k);
-  const float y = D > 0.f ? O / D : 0.f;
-  if constexpr (DT == DT_BF16) {
-    reinterpret_cast<unsigned short*>(out)[(size_t)row * kHeadDim + lane] = to_bf16(y);
-  } else {
-    reinterpret_cast<float*>(out)[(size_t)row * kHeadDim + lane] = y;
+    for (int k = 1; k < CL; ++k) sum += sm_o[rl][k][dq];
+    const float D = sm_D[rl];
+    float y[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) y[i] = D > 0.f ? sum[i] / D : 0.f;
+    const size_t off = (size_t)row * kHeadDim + 4 * dq;
+    if constexpr (DT == DT_BF16) {
+      *reinterpret_cast<u32x2*>(out + off * 2) = u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+    } else {
+      *reinterpret_cast<f32x4*>(out + off * 4) = f32x4{y[0], y[1], y[2], y[3]};
+    }
   }
 }
 
@@ -422,15 +486,21 @@ __global__ __launch_bounds__(256, PrefillCfg<DT>::MIN_BLOCKS) void prefill_kerne
     const char* __restrict__ q, const char* __restrict__ k, const char* __restrict__ v,
     const float* __restrict__ sinks, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ cu_kv, int total_q, int total_kv, int hkv, int group,
-    float qk_scale_log2, int causal, int n_qtiles, char* __restrict__ out) {
+    float qk_scale_log2, int causal, int n_qtiles, int n_pairs, char* __restrict__ out) {
   using Cfg = PrefillCfg<DT>;
   constexpr int ES = Cfg::ES, KROW = Cfg::KROW, VROW = Cfg::VROW;
   constexpr int BK = 64;  // keys per tile
   __shared__ __attribute__((aligned(16))) char lds_k[2][BK * KROW * ES];
   __shared__ __attribute__((aligned(16))) char lds_v[2][kHeadDim * VROW * ES];
 
-  const int b = blockIdx.z, kvh = blockIdx.y;
-  const int tile = n_qtiles - 1 - (int)blockIdx.x;  // longest causal tiles first
+  // 1-D grid, (sequence, kv head) pair fastest and query tiles from the last
+  // (longest causal key range) to the first: the dispatcher hands out the
+  // heaviest work first, and with a pair count that is a multiple of the 8
+  // XCDs (workgroups go round-robin over XCDs) every tile of a pair lands on
+  // the same XCD, whose L2 then holds that pair's K/V.
+  const int pair = (int)(blockIdx.x % (unsigned)n_pairs);
+  const int tile = n_qtiles - 1 - (int)(blockIdx.x / (unsigned)n_pairs);
+  const int kvh = pair % hkv, b = pair / hkv;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, col = lane & 31;
@@ -593,7 +663,11 @@ __global__ __launch_bounds__(256, PrefillCfg<DT>::MIN_BLOCKS) void prefill_kerne
       }
     }
 
-    // online softmax per row block
+    // Online softmax per row block.  The reference max m_run is raised only
+    // when a row's tile max exceeds it by more than kRescaleLog2 (then O and d
+    // are rescaled, a wave-uniform and rarely taken branch); otherwise the
+    // stale m_run is kept and p = 2^(x - m_run) stays below 2^kRescaleLog2.
+    // The normalised result O/d does not depend on which reference is used.
     const bool need_mask = (jt * BK + BK - 1) > lim_min;
     u32x4 pf[2][2][2];  // bf16 P^T operands [rb][kb][half]
 #pragma unroll
@@ -607,36 +681,54 @@ __global__ __launch_bounds__(256, PrefillCfg<DT>::MIN_BLOCKS) void prefill_kerne
             if (key > lim[rb]) sacc[kb][rb][r] = kNegInf;
           }
       }
-      float mx = kNegInf;
+      float mx4[4] = {kNegInf, kNegInf, kNegInf, kNegInf};  // 4 chains of max3
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][rb][r]);
-      mx = xor_max(mx, 32);
-      const float m_new = fmaxf(m_run[rb], mx * qk_scale_log2);
-      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run[rb] - m_use);
-      float psum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pr = fast_exp2(__builtin_fmaf(sacc[kb][rb][r], qk_scale_log2, -m_use));
-          sacc[kb][rb][r] = pr;
-          psum += pr;
+        for (int r = 0; r < 16; r += 2) {
+          float& a = mx4[(kb * 8 + r / 2) & 3];
+          a = fmaxf(fmaxf(a, sacc[kb][rb][r]), sacc[kb][rb][r + 1]);
         }
-      d_run[rb] = d_run[rb] * alpha + psum;
-      m_run[rb] = m_new;
+      float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
+      mx = xor_max(mx, 32) * qk_scale_log2;
+      const bool grow = mx > m_run[rb] + kRescaleLog2;
+      if (wave_any(grow)) {
+        // only rows that crossed the threshold move their reference (others
+        // scale by exactly 1), so a row's result never depends on other rows
+        const float alpha = grow ? fast_exp2(m_run[rb] - mx) : 1.f;
+        d_run[rb] *= alpha;
 #pragma unroll
-      for (int db = 0; db < 2; ++db) acc_o[db][rb] *= alpha;
+        for (int db = 0; db < 2; ++db) acc_o[db][rb] *= alpha;
+        m_run[rb] = grow ? mx : m_run[rb];
+      }
+      const float m_use = (m_run[rb] == kNegInf) ? 0.f : m_run[rb];
       if constexpr (DT == DT_BF16) {
+        float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              pf[rb][kb][hh][e] = pack_bf16x2(sacc[kb][rb][8 * hh + 2 * e], sacc[kb][rb][8 * hh + 2 * e + 1]);
+            for (int e = 0; e < 4; ++e) {
+              const int r = 8 * hh + 2 * e;
+              const float p0 = fast_exp2(__builtin_fmaf(sacc[kb][rb][r], qk_scale_log2, -m_use));
+              const float p1 = fast_exp2(__builtin_fmaf(sacc[kb][rb][r + 1], qk_scale_log2, -m_use));
+              const unsigned int pk = pack_bf16x2(p0, p1);
+              pf[rb][kb][hh][e] = pk;
+              ps[e] = add_bf16x2(pk, ps[e]);
+            }
+        d_run[rb] += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+      } else {
+        float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float pr = fast_exp2(__builtin_fmaf(sacc[kb][rb][r], qk_scale_log2, -m_use));
+            sacc[kb][rb][r] = pr;
+            ps[r & 3] += pr;
+          }
+        d_run[rb] += (ps[0] + ps[1]) + (ps[2] + ps[3]);
       }
     }
 
@@ -722,8 +814,16 @@ int launch_status() {
   return hipGetLastError() == hipSuccess ? ATTN_SINK_OK : ATTN_SINK_ERR_LAUNCH;
 }
 
-constexpr int kDecodeWaves = 4;
-constexpr int kDecodeUnroll = 4;
+// Decode workgroup shape: waves per workgroup and pages per register group
+// (two groups are in flight per wave).
+#ifndef ATTN_SINK_DECODE_WAVES
+#define ATTN_SINK_DECODE_WAVES 4
+#endif
+#ifndef ATTN_SINK_DECODE_UNROLL
+#define ATTN_SINK_DECODE_UNROLL 2
+#endif
+constexpr int kDecodeWaves = ATTN_SINK_DECODE_WAVES;
+constexpr int kDecodeUnroll = ATTN_SINK_DECODE_UNROLL;
 
 }  // namespace
 
@@ -756,7 +856,7 @@ int attn_sink_prefill(const void* q, const void* k, const void* v, const float* 
       (dtype != ATTN_SINK_F32 && dtype != ATTN_SINK_BF16) || !finite_positive(sm_scale))
     return ATTN_SINK_ERR_INVALID_ARG;
   if (head_dim != kHeadDim || group_size > 64) return ATTN_SINK_ERR_UNSUPPORTED;
-  if (batch > 65535 || num_kv_heads > 65535) return ATTN_SINK_ERR_UNSUPPORTED;
+  if ((int64_t)batch * num_kv_heads > INT32_MAX) return ATTN_SINK_ERR_UNSUPPORTED;
   const int es = dtype == ATTN_SINK_BF16 ? 2 : 4;
   const int64_t hq = (int64_t)num_kv_heads * group_size;
   // buffer offsets are 32-bit: each whole tensor must stay below 4 GiB
@@ -766,19 +866,21 @@ int attn_sink_prefill(const void* q, const void* k, const void* v, const float* 
   if (batch == 0 || total_q == 0 || max_seqlen_q == 0) return ATTN_SINK_OK;
   const int tb = 4 * (64 / group_size);
   const int n_qtiles = (max_seqlen_q + tb - 1) / tb;
-  const dim3 grid(n_qtiles, num_kv_heads, batch);
+  const int n_pairs = batch * num_kv_heads;
+  if ((int64_t)n_qtiles * n_pairs > INT32_MAX) return ATTN_SINK_ERR_UNSUPPORTED;
+  const dim3 grid(n_qtiles * n_pairs);
   const float qk = sm_scale * kLog2e;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (dtype == ATTN_SINK_BF16)
     hipLaunchKernelGGL(prefill_kernel<DT_BF16>, grid, dim3(256), 0, s, (const char*)q,
                        (const char*)k, (const char*)v, sinks, cu_seqlens_q, cu_seqlens_kv,
                        total_q, total_kv, num_kv_heads, group_size, qk, causal, n_qtiles,
-                       (char*)out);
+                       n_pairs, (char*)out);
   else
     hipLaunchKernelGGL(prefill_kernel<DT_F32>, grid, dim3(256), 0, s, (const char*)q,
                        (const char*)k, (const char*)v, sinks, cu_seqlens_q, cu_seqlens_kv,
                        total_q, total_kv, num_kv_heads, group_size, qk, causal, n_qtiles,
-                       (char*)out);
+                       n_pairs, (char*)out);
   return launch_status();
 }
 
@@ -840,16 +942,25 @@ int attn_sink_merge(const float* partial_m, const float* partial_d, const float*
     return ATTN_SINK_ERR_INVALID_ARG;
   if (head_dim != kHeadDim) return ATTN_SINK_ERR_UNSUPPORTED;
   const int64_t rows = (int64_t)batch * num_q_heads;
-  if (rows > INT32_MAX - 3) return ATTN_SINK_ERR_UNSUPPORTED;
+  if (rows > INT32_MAX - 16) return ATTN_SINK_ERR_UNSUPPORTED;
   if (rows == 0) return ATTN_SINK_OK;
-  const dim3 grid((unsigned)((rows + 3) / 4));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (out_dtype == ATTN_SINK_BF16)
-    hipLaunchKernelGGL(merge_kernel<DT_BF16>, grid, dim3(256), 0, s, partial_m, partial_d,
-                       partial_o, (int)rows, num_splits, (char*)out);
-  else
-    hipLaunchKernelGGL(merge_kernel<DT_F32>, grid, dim3(256), 0, s, partial_m, partial_d,
-                       partial_o, (int)rows, num_splits, (char*)out);
+  const bool bf = out_dtype == ATTN_SINK_BF16;
+  // chunk lanes per row: up to 16, fewer when there are fewer splits
+  const int cl = num_splits >= 16 ? 16 : num_splits >= 8 ? 8 : num_splits >= 4 ? 4 : 2;
+  const int rpb = 256 / (16 * cl);
+  const dim3 grid((unsigned)((rows + rpb - 1) / rpb));
+#define ATTN_SINK_MERGE(CLV)                                                                  \
+  hipLaunchKernelGGL((bf ? merge_kernel<DT_BF16, CLV> : merge_kernel<DT_F32, CLV>), grid,      \
+                     dim3(256), 0, s, partial_m, partial_d, partial_o, (int)rows, num_splits,  \
+                     (char*)out)
+  switch (cl) {
+    case 16: ATTN_SINK_MERGE(16); break;
+    case 8: ATTN_SINK_MERGE(8); break;
+    case 4: ATTN_SINK_MERGE(4); break;
+    default: ATTN_SINK_MERGE(2); break;
+  }
+#undef ATTN_SINK_MERGE
   return launch_status();
 }
 
