@@ -55,6 +55,25 @@ def decode_bytes(kv_lens, hq, hkv, dim, splits, es=2):
     return dict(total=kv + q_o + pages + 2 * partials, decode=decode, merge=merge, kv=kv)
 
 
+def counted_traffic():
+    """Per-launch HBM bytes measured with rocprofv3 FETCH_SIZE/WRITE_SIZE (scaled
+    by a plain copy of known size), kept in profiles/hbm_traffic.json together
+    with the hash of the kernel source they were taken on.  Returns None when
+    the kernels have changed since (the figures no longer describe them)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    src = os.path.join(ROOT, "gqa_attention_sinks_initialised_amd", "csrc", "attn_sink.hip")
+    try:
+        rec = json.load(open(path))
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != sha:
+        return None
+    return {k: v.get("fetch_bytes", 0.0) + v.get("write_bytes", 0.0)
+            for k, v in rec.get("per_launch_bytes", {}).items()}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -63,11 +82,23 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy 5 times (reference for the "
+                         "HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only; run with --gpus 1 "
               "(the multi-GPU split of this path is described, not built)", file=sys.stderr)
         sys.exit(2)
+    if args.calibrate_copy:
+        import torch
+        src = torch.ones(1 << 28, device="cuda:0", dtype=torch.float32)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": 1 << 30, "bytes_written": 1 << 30}))
+        return
 
     import torch
     import gqa_attention_sinks_initialised_amd as attn
@@ -156,6 +187,7 @@ def main():
     gbs3_k = b3["decode"] / (t["decode"] * 1e-3) / 1e9
     gbs4_k = b4["decode"] / (t["split"] * 1e-3) / 1e9
 
+    traffic = counted_traffic() or {}
     result = {
         "metric": "prefill attention TFLOP/s (bf16) + decode KV-read HBM GB/s, % of roofline",
         "value": round(tflops, 2),
@@ -175,7 +207,8 @@ def main():
                    "prefill_tokens": 8192, "decode_splits": s3, "split_splits": s4},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic.get("prefill"),
                      "kernel": "prefill_kernel<bf16>", "flops_per_launch": fl2,
                      "us_per_launch": round(t["prefill"] * 1e3, 2)},
         "decode": {"workload": c3["name"], "splits": s3,
@@ -184,14 +217,16 @@ def main():
                    "bytes": b3["total"], "GB/s": round(gbs3, 1),
                    "frac": round(gbs3 / PEAK_HBM_GBS, 4),
                    "decode_kernel_GB/s": round(gbs3_k, 1),
-                   "decode_kernel_frac": round(gbs3_k / PEAK_HBM_GBS, 4)},
+                   "decode_kernel_frac": round(gbs3_k / PEAK_HBM_GBS, 4),
+                   "traffic": traffic.get("decode_paged")},
         "split_decode": {"workload": c4["name"], "splits": s4,
                          "us_decode": round(t["split"] * 1e3, 2),
                          "us_merge": round(t["split_merge"] * 1e3, 2),
                          "bytes": b4["total"], "GB/s": round(gbs4, 1),
                          "frac": round(gbs4 / PEAK_HBM_GBS, 4),
                          "decode_kernel_GB/s": round(gbs4_k, 1),
-                         "decode_kernel_frac": round(gbs4_k / PEAK_HBM_GBS, 4)},
+                         "decode_kernel_frac": round(gbs4_k / PEAK_HBM_GBS, 4),
+                         "traffic": traffic.get("decode_split")},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(c2, args.cpu_seconds)
