@@ -38,6 +38,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+
 #include "attn_sink.h"
 
 namespace {
@@ -450,45 +451,46 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pm
 
 // =========================================================== prefill kernel
 //
-// Workgroup = 4 waves; wave w owns 64 rows, row r = (token r / G, head r % G)
-// of tokens [t_begin + w*TW, +TW), TW = 64 / G.  Key tiles of 64 are staged
-// in LDS (K row-major, V transposed to dim-major) with a double buffer: the
-// next tile's global loads are in flight while the current tile is used.
-// Per tile and wave:
-//   S^T[64 keys x 64 rows]  = K . Q^T       (2 key blocks x 2 row blocks)
-//   O^T[64 dims x 64 rows] += V^T . P^T     (2 dim blocks x 2 row blocks)
+// Workgroup = WAVES waves; wave w owns ROWS = 32*RB rows, row r = (token
+// r / G, head r % G) of tokens [t_begin + w*TW, +TW), TW = ROWS / G, so every
+// query head of a kv group reads the same K/V tile.  Key tiles of 64 are
+// staged in LDS (K row-major, V transposed to dim-major) with a double
+// buffer: the next tile's global loads are in flight while the current tile
+// is used.  Per tile and wave:
+//   S^T[64 keys x ROWS]  = K . Q^T       (2 key blocks x RB row blocks)
+//   O^T[64 dims x ROWS] += V^T . P^T     (2 dim blocks x RB row blocks)
 // A 32x32 MFMA result gives lane l column l%32 (a row) and the 16 rows
 // 8*(r/4) + 4*(l/32) + r%4, r = 0..15 (keys for S^T, dims for O^T).  Each
 // row's 64 keys are thus split over lanes l and l^32; its max is one
-// cross-lane exchange and its sum is deferred to the end.
+// cross-lane exchange and its sum is deferred to the end.  The register
+// layout of S^T is directly the P^T operand of the next product (same key
+// order on the V side), so no shuffle sits between the two products.
 
-template <int DT>
-struct PrefillCfg;
-
-template <>
-struct PrefillCfg<DT_BF16> {
-  static constexpr int ES = 2;
-  static constexpr int KROW = kHeadDim + 8;  // elements per LDS K row (pad 16 B)
-  static constexpr int VROW = 64 + 4;        // elements per LDS Vt row (pad 8 B)
-  static constexpr int MIN_BLOCKS = 2;
+// LDS tiles.  bf16: K and V both row-major with unpadded 128-byte rows,
+// XOR-swizzled at 16-byte-chunk granularity (K chunk c of row r at slot
+// c ^ (r & 7), V chunk c at slot c ^ 2*(r & 3)); V^T operands are read with
+// ds_read_b64_tr_b16.  fp32: K row-major and V transposed (dim-major), rows
+// padded by 16 bytes.
+template <int DT, int RB, int WAVES>
+struct PrefillCfg {
+  static constexpr int ES = DT == DT_BF16 ? 2 : 4;
+  static constexpr int KROW = kHeadDim + (DT == DT_BF16 ? 0 : 4);  // LDS K row (elements)
+  static constexpr int VROW = 64 + (DT == DT_BF16 ? 0 : 4);         // LDS V / Vt row
+  static constexpr int NT = 64 * WAVES;
+  static constexpr int ROWS = 32 * RB;
+  // registers allow 2 waves per SIMD for 64-row bf16 waves, more for 32 rows
+  static constexpr int MIN_WAVES_PER_EU = DT == DT_F32 ? 1 : (RB == 2 ? 2 : 3);
 };
 
-template <>
-struct PrefillCfg<DT_F32> {
-  static constexpr int ES = 4;
-  static constexpr int KROW = kHeadDim + 4;
-  static constexpr int VROW = 64 + 4;
-  static constexpr int MIN_BLOCKS = 1;
-};
-
-template <int DT>
-__global__ __launch_bounds__(256, PrefillCfg<DT>::MIN_BLOCKS) void prefill_kernel(
-    const char* __restrict__ q, const char* __restrict__ k, const char* __restrict__ v,
-    const float* __restrict__ sinks, const int32_t* __restrict__ cu_q,
-    const int32_t* __restrict__ cu_kv, int total_q, int total_kv, int hkv, int group,
-    float qk_scale_log2, int causal, int n_qtiles, int n_pairs, char* __restrict__ out) {
-  using Cfg = PrefillCfg<DT>;
-  constexpr int ES = Cfg::ES, KROW = Cfg::KROW, VROW = Cfg::VROW;
+template <int DT, int RB, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, (PrefillCfg<DT, RB, WAVES>::MIN_WAVES_PER_EU)) void
+prefill_kernel(const char* __restrict__ q, const char* __restrict__ k, const char* __restrict__ v,
+               const float* __restrict__ sinks, const int32_t* __restrict__ cu_q,
+               const int32_t* __restrict__ cu_kv, int total_q, int total_kv, int hkv, int group,
+               float qk_scale_log2, int causal, int n_qtiles, int n_pairs,
+               char* __restrict__ out) {
+  using Cfg = PrefillCfg<DT, RB, WAVES>;
+  constexpr int ES = Cfg::ES, KROW = Cfg::KROW, VROW = Cfg::VROW, NT = Cfg::NT;
   constexpr int BK = 64;  // keys per tile
   __shared__ __attribute__((aligned(16))) char lds_k[2][BK * KROW * ES];
   __shared__ __attribute__((aligned(16))) char lds_v[2][kHeadDim * VROW * ES];
@@ -505,8 +507,8 @@ __global__ __launch_bounds__(256, PrefillCfg<DT>::MIN_BLOCKS) void prefill_kerne
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, col = lane & 31;
   const int hq = hkv * group;
-  const int TW = 64 / group;  // tokens per wave
-  const int TB = 4 * TW;      // tokens per workgroup
+  const int TW = Cfg::ROWS / group;  // tokens per wave
+  const int TB = WAVES * TW;         // tokens per workgroup
 
   const int q0 = clampi(cu_q[b], 0, total_q), q1 = clampi(cu_q[b + 1], q0, total_q);
   const int k0 = clampi(cu_kv[b], 0, total_kv), k1 = clampi(cu_kv[b + 1], k0, total_kv);
@@ -516,17 +518,17 @@ __global__ __launch_bounds__(256, PrefillCfg<DT>::MIN_BLOCKS) void prefill_kerne
   const int t_last = min(t_begin + TB, Lq) - 1;
   const int shift = Lkv - Lq;  // bottom-right causal alignment
 
-  // keys this workgroup needs, and the first tile that needs masking
+  // keys this workgroup needs, and the key below which no valid row masks
   int n_keys = causal ? min(Lkv, t_last + shift + 1) : Lkv;
   n_keys = max(n_keys, 0);
   const int n_tiles = (n_keys + BK - 1) / BK;
   const int lim_min = causal ? min(t_begin + shift, Lkv - 1) : Lkv - 1;
 
-  // ---- rows of this lane: rb = 0, 1
-  int lim[2], head[2], tok[2];
-  bool valid[2];
+  // ---- rows of this lane, one per row block
+  int lim[RB], head[RB], tok[RB];
+  bool valid[RB];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < RB; ++rb) {
     const int r = 32 * rb + col;
     const int tl = r / group, hl = r - tl * group;
     tok[rb] = t_begin + w * TW + tl;
@@ -539,29 +541,30 @@ __global__ __launch_bounds__(256, PrefillCfg<DT>::MIN_BLOCKS) void prefill_kerne
   const __amdgpu_buffer_rsrc_t qr =
       make_rsrc(q + (size_t)q0 * hq * kHeadDim * ES, (uint32_t)((size_t)Lq * hq * kHeadDim * ES));
   constexpr int QV = DT == DT_BF16 ? 4 : 8;  // 16-byte vectors per lane per row
-  u32x4 qf[2][QV];
+  u32x4 qf[RB][QV];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < RB; ++rb) {
     const uint32_t base = ((uint32_t)tok[rb] * hq + head[rb]) * kHeadDim * ES + 32 * g * ES;
 #pragma unroll
     for (int s = 0; s < QV; ++s)
       qf[rb][s] = valid[rb] ? buf_load16(qr, base + 16 * s) : u32x4{0, 0, 0, 0};
   }
 
-  // ---- running state per row (log2 units); the sink is counted in lane
-  // group 0 only, since d is summed over the two lanes of a row at the end
-  float m_run[2], d_run[2];
+  // ---- running state per row (log2 units), starting from the sink: m = s,
+  // d = e^(s - m) = 1 (0 for s = -inf), counted in lane group 0 only because
+  // d is summed over the two lanes of a row at the end
+  float m_run[RB], d_run[RB];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < RB; ++rb) {
     const float s = valid[rb] ? sinks[head[rb]] : kNegInf;
     m_run[rb] = s * kLog2e;
     d_run[rb] = (g == 0 && s != kNegInf) ? 1.f : 0.f;
   }
-  f32x16 acc_o[2][2];
+  f32x16 acc_o[2][RB];
 #pragma unroll
   for (int db = 0; db < 2; ++db)
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc_o[db][rb][i] = 0.f;
 
@@ -571,29 +574,31 @@ __global__ __launch_bounds__(256, PrefillCfg<DT>::MIN_BLOCKS) void prefill_kerne
       make_rsrc(k + (size_t)k0 * kv_row_bytes, (uint32_t)((size_t)Lkv * kv_row_bytes));
   const __amdgpu_buffer_rsrc_t vr =
       make_rsrc(v + (size_t)k0 * kv_row_bytes, (uint32_t)((size_t)Lkv * kv_row_bytes));
-  constexpr int CPR = kHeadDim * ES / 16;      // 16-byte chunks per key row
-  constexpr int NCH = BK * CPR / 256;          // chunks per thread per tile (K, and V)
-  u32x4 stk[NCH], stv[NCH];
+  constexpr int CPR = kHeadDim * ES / 16;             // 16-byte chunks per key row
+  constexpr int NCH = (BK * CPR + NT - 1) / NT;       // K chunks per thread
+  constexpr int VITEMS = BK * CPR;                    // V chunks (one key row each)
+  constexpr int NCV = (VITEMS + NT - 1) / NT;
+  constexpr int VREG = 1;
+  u32x4 stk[NCH], stv[NCV][VREG];
+  const uint32_t head_off = (uint32_t)kvh * kHeadDim * ES;
 
   auto stage_load = [&](int jt) {
     const int key0 = jt * BK;
-    if constexpr (DT == DT_BF16) {
 #pragma unroll
-      for (int u = 0; u < NCH; ++u) {  // K: chunk c -> key c / 8, part c % 8
-        const int c = tid + 256 * u, key = c / CPR, part = c % CPR;
-        stk[u] = buf_load16(kr, (uint32_t)(key0 + key) * kv_row_bytes + kvh * kHeadDim * ES + part * 16);
-      }
-      // V: thread -> key pair kp = tid / 8, part tid % 8; keys 2kp and 2kp+1
-      const int kp = tid / CPR, part = tid % CPR;
+    for (int u = 0; u < NCH; ++u) {
+      const int c = tid + NT * u, key = c / CPR, part = c % CPR;
+      if (c < BK * CPR)
+        stk[u] = buf_load16(kr, (uint32_t)(key0 + key) * kv_row_bytes + head_off + part * 16);
+    }
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
-        stv[u] = buf_load16(vr, (uint32_t)(key0 + 2 * kp + u) * kv_row_bytes + kvh * kHeadDim * ES + part * 16);
-    } else {
+    for (int u = 0; u < NCV; ++u) {
+      const int c = tid + NT * u, part = c % CPR;
+      if (c < VITEMS) {
 #pragma unroll
-      for (int u = 0; u < NCH; ++u) {
-        const int c = tid + 256 * u, key = c / CPR, part = c % CPR;
-        stk[u] = buf_load16(kr, (uint32_t)(key0 + key) * kv_row_bytes + kvh * kHeadDim * ES + part * 16);
-        stv[u] = buf_load16(vr, (uint32_t)(key0 + key) * kv_row_bytes + kvh * kHeadDim * ES + part * 16);
+        for (int x = 0; x < VREG; ++x) {
+          const int key = (c / CPR) * VREG + x;
+          stv[u][x] = buf_load16(vr, (uint32_t)(key0 + key) * kv_row_bytes + head_off + part * 16);
+        }
       }
     }
   };
@@ -601,29 +606,28 @@ __global__ __launch_bounds__(256, PrefillCfg<DT>::MIN_BLOCKS) void prefill_kerne
   auto stage_store = [&](int buf) {
     char* kd = lds_k[buf];
     char* vd = lds_v[buf];
-    if constexpr (DT == DT_BF16) {
 #pragma unroll
-      for (int u = 0; u < NCH; ++u) {
-        const int c = tid + 256 * u, key = c / CPR, part = c % CPR;
-        *reinterpret_cast<u32x4*>(kd + (key * KROW + part * 8) * ES) = stk[u];
+    for (int u = 0; u < NCH; ++u) {
+      const int c = tid + NT * u, key = c / CPR, part = c % CPR;
+      if (c < BK * CPR) {
+        if constexpr (DT == DT_BF16)
+          *reinterpret_cast<u32x4*>(kd + key * 128 + 16 * (part ^ (key & 7))) = stk[u];
+        else
+          *reinterpret_cast<u32x4*>(kd + (key * KROW + part * (16 / ES)) * ES) = stk[u];
       }
-      const int kp = tid / CPR, part = tid % CPR;
-      // Vt[dim][key]: word (V[2kp][dim], V[2kp+1][dim]) for dims 8*part + i
+    }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const unsigned int a = stv[0][i >> 1], bb = stv[1][i >> 1];
-        const unsigned int word = (i & 1) ? ((a >> 16) | (bb & 0xffff0000u))
-                                          : ((a & 0xffffu) | (bb << 16));
-        *reinterpret_cast<unsigned int*>(vd + ((8 * part + i) * VROW + 2 * kp) * ES) = word;
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < NCH; ++u) {
-        const int c = tid + 256 * u, key = c / CPR, part = c % CPR;
-        *reinterpret_cast<u32x4*>(kd + (key * KROW + part * 4) * ES) = stk[u];
+    for (int u = 0; u < NCV; ++u) {
+      const int c = tid + NT * u, part = c % CPR;
+      if (c >= VITEMS) continue;
+      if constexpr (DT == DT_BF16) {
+        const int key = c / CPR;
+        *reinterpret_cast<u32x4*>(vd + key * 128 + 16 * (part ^ (2 * (key & 3)))) = stv[u][0];
+      } else {
+        const int key = c / CPR;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          *reinterpret_cast<unsigned int*>(vd + ((4 * part + i) * VROW + key) * ES) = stv[u][i];
+          *reinterpret_cast<unsigned int*>(vd + ((4 * part + i) * VROW + key) * ES) = stv[u][0][i];
       }
     }
   };
@@ -631,24 +635,29 @@ __global__ __launch_bounds__(256, PrefillCfg<DT>::MIN_BLOCKS) void prefill_kerne
   auto compute_tile = [&](int buf, int jt) {
     const char* kd = lds_k[buf];
     const char* vd = lds_v[buf];
-    f32x16 sacc[2][2];
+    f32x16 sacc[2][RB];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
+      for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) sacc[kb][rb][i] = 0.f;
 
     // S^T = K Q^T
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      const int krw = kb * 32 + col;
       const char* krow = kd + ((kb * 32 + col) * KROW + 32 * g) * ES;
 #pragma unroll
       for (int s = 0; s < QV; ++s) {
-        const u32x4 kf = *reinterpret_cast<const u32x4*>(krow + 16 * s);
+        u32x4 kf;
+        if constexpr (DT == DT_BF16)
+          kf = *reinterpret_cast<const u32x4*>(kd + krw * 128 + 16 * ((4 * g + s) ^ (krw & 7)));
+        else
+          kf = *reinterpret_cast<const u32x4*>(krow + 16 * s);
         if constexpr (DT == DT_BF16) {
 #pragma unroll
-          for (int rb = 0; rb < 2; ++rb)
+          for (int rb = 0; rb < RB; ++rb)
             sacc[kb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                 __builtin_bit_cast(bf16x8, kf), __builtin_bit_cast(bf16x8, qf[rb][s]),
                 sacc[kb][rb], 0, 0, 0);
@@ -656,22 +665,22 @@ __global__ __launch_bounds__(256, PrefillCfg<DT>::MIN_BLOCKS) void prefill_kerne
 #pragma unroll
           for (int e = 0; e < 4; ++e)
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
+            for (int rb = 0; rb < RB; ++rb)
               sacc[kb][rb] = __builtin_amdgcn_mfma_f32_32x32x2f32(
                   __uint_as_float(kf[e]), __uint_as_float(qf[rb][s][e]), sacc[kb][rb], 0, 0, 0);
         }
       }
     }
 
-    // Online softmax per row block.  The reference max m_run is raised only
-    // when a row's tile max exceeds it by more than kRescaleLog2 (then O and d
-    // are rescaled, a wave-uniform and rarely taken branch); otherwise the
-    // stale m_run is kept and p = 2^(x - m_run) stays below 2^kRescaleLog2.
-    // The normalised result O/d does not depend on which reference is used.
+    // Online softmax.  The reference max m_run is raised only when a row's
+    // tile max exceeds it by more than kRescaleLog2 (then only that row's O
+    // and d are rescaled, in a wave-uniform, rarely taken branch); otherwise
+    // p = 2^(x - m_run) stays below 2^kRescaleLog2.  O/d does not depend on
+    // which reference is used.
     const bool need_mask = (jt * BK + BK - 1) > lim_min;
-    u32x4 pf[2][2][2];  // bf16 P^T operands [rb][kb][half]
+    u32x4 pf[RB][2][2];  // bf16 P^T operands [rb][kb][half]
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+    for (int rb = 0; rb < RB; ++rb) {
       if (need_mask) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -689,8 +698,8 @@ __global__ __launch_bounds__(256, PrefillCfg<DT>::MIN_BLOCKS) void prefill_kerne
           float& a = mx4[(kb * 8 + r / 2) & 3];
           a = fmaxf(fmaxf(a, sacc[kb][rb][r]), sacc[kb][rb][r + 1]);
         }
-      float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
-      mx = xor_max(mx, 32) * qk_scale_log2;
+      const float mx =
+          xor_max(fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3])), 32) * qk_scale_log2;
       const bool grow = mx > m_run[rb] + kRescaleLog2;
       if (wave_any(grow)) {
         // only rows that crossed the threshold move their reference (others
@@ -702,8 +711,8 @@ __global__ __launch_bounds__(256, PrefillCfg<DT>::MIN_BLOCKS) void prefill_kerne
         m_run[rb] = grow ? mx : m_run[rb];
       }
       const float m_use = (m_run[rb] == kNegInf) ? 0.f : m_run[rb];
+      float ps[4] = {0.f, 0.f, 0.f, 0.f};
       if constexpr (DT == DT_BF16) {
-        float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -717,9 +726,7 @@ __global__ __launch_bounds__(256, PrefillCfg<DT>::MIN_BLOCKS) void prefill_kerne
               pf[rb][kb][hh][e] = pk;
               ps[e] = add_bf16x2(pk, ps[e]);
             }
-        d_run[rb] += (ps[0] + ps[1]) + (ps[2] + ps[3]);
       } else {
-        float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -728,8 +735,8 @@ __global__ __launch_bounds__(256, PrefillCfg<DT>::MIN_BLOCKS) void prefill_kerne
             sacc[kb][rb][r] = pr;
             ps[r & 3] += pr;
           }
-        d_run[rb] += (ps[0] + ps[1]) + (ps[2] + ps[3]);
       }
+      d_run[rb] += (ps[0] + ps[1]) + (ps[2] + ps[3]);
     }
 
     // O^T += V^T P^T
@@ -739,14 +746,24 @@ __global__ __launch_bounds__(256, PrefillCfg<DT>::MIN_BLOCKS) void prefill_kerne
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         if constexpr (DT == DT_BF16) {
+          // source lane s of each 16-lane group points at V[kbase + s/4][dim0 +
+          // 4*(s%4)]; after the transposing read lane i holds V[kbase + 0..3]
+          // [dim0 + i] with dim0 + i = 32*db + lane%32
+          typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+          const int sl = lane & 15;
+          const int dim = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (sl & 3);
+          const int chunk = dim >> 3, sub = 2 * (dim & 7);
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
-            const int key = kb * 32 + 16 * hh + 4 * g;
-            const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + key * ES);
-            const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + (key + 8) * ES);
+            const int r0 = kb * 32 + 16 * hh + 4 * g + (sl >> 2), r1 = r0 + 8;
+            const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4*)(vd + r0 * 128 + 16 * (chunk ^ (2 * (r0 & 3))) + sub));
+            const i16x4 c = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4*)(vd + r1 * 128 + 16 * (chunk ^ (2 * (r1 & 3))) + sub));
+            const u32x2 lo = __builtin_bit_cast(u32x2, a), hi = __builtin_bit_cast(u32x2, c);
             const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
+            for (int rb = 0; rb < RB; ++rb)
               acc_o[db][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                   __builtin_bit_cast(bf16x8, vf), __builtin_bit_cast(bf16x8, pf[rb][kb][hh]),
                   acc_o[db][rb], 0, 0, 0);
@@ -759,7 +776,7 @@ __global__ __launch_bounds__(256, PrefillCfg<DT>::MIN_BLOCKS) void prefill_kerne
 #pragma unroll
             for (int e = 0; e < 4; ++e)
 #pragma unroll
-              for (int rb = 0; rb < 2; ++rb)
+              for (int rb = 0; rb < RB; ++rb)
                 acc_o[db][rb] = __builtin_amdgcn_mfma_f32_32x32x2f32(
                     __uint_as_float(vf[e]), sacc[kb][rb][4 * qd + e], acc_o[db][rb], 0, 0, 0);
           }
@@ -783,7 +800,7 @@ __global__ __launch_bounds__(256, PrefillCfg<DT>::MIN_BLOCKS) void prefill_kerne
 
   // ---- epilogue: out = O / d, rows of this lane, dims 32db + 8qd + 4g + 0..3
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < RB; ++rb) {
     const float dsum = xor_sum(d_run[rb], 32);
     if (!valid[rb]) continue;
     const float inv = dsum > 0.f ? 1.f / dsum : 0.f;
@@ -864,20 +881,20 @@ int attn_sink_prefill(const void* q, const void* k, const void* v, const float* 
       (int64_t)total_kv * num_kv_heads * kHeadDim * es >= (int64_t)1 << 32)
     return ATTN_SINK_ERR_UNSUPPORTED;
   if (batch == 0 || total_q == 0 || max_seqlen_q == 0) return ATTN_SINK_OK;
-  const int tb = 4 * (64 / group_size);
-  const int n_qtiles = (max_seqlen_q + tb - 1) / tb;
-  const int n_pairs = batch * num_kv_heads;
-  if ((int64_t)n_qtiles * n_pairs > INT32_MAX) return ATTN_SINK_ERR_UNSUPPORTED;
-  const dim3 grid(n_qtiles * n_pairs);
   const float qk = sm_scale * kLog2e;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (dtype == ATTN_SINK_BF16)
-    hipLaunchKernelGGL(prefill_kernel<DT_BF16>, grid, dim3(256), 0, s, (const char*)q,
+  const int n_pairs = batch * num_kv_heads;
+  const int tb = 4 * (64 / group_size);  // 4 waves of 64 rows
+  const int n_qtiles = (max_seqlen_q + tb - 1) / tb;
+  if ((int64_t)n_qtiles * n_pairs > INT32_MAX) return ATTN_SINK_ERR_UNSUPPORTED;
+  const dim3 grid(n_qtiles * n_pairs);
+  if (dtype == ATTN_SINK_F32)
+    hipLaunchKernelGGL((prefill_kernel<DT_F32, 2, 4>), grid, dim3(256), 0, s, (const char*)q,
                        (const char*)k, (const char*)v, sinks, cu_seqlens_q, cu_seqlens_kv,
                        total_q, total_kv, num_kv_heads, group_size, qk, causal, n_qtiles,
                        n_pairs, (char*)out);
   else
-    hipLaunchKernelGGL(prefill_kernel<DT_F32>, grid, dim3(256), 0, s, (const char*)q,
+    hipLaunchKernelGGL((prefill_kernel<DT_BF16, 2, 4>), grid, dim3(256), 0, s, (const char*)q,
                        (const char*)k, (const char*)v, sinks, cu_seqlens_q, cu_seqlens_kv,
                        total_q, total_kv, num_kv_heads, group_size, qk, causal, n_qtiles,
                        n_pairs, (char*)out);
