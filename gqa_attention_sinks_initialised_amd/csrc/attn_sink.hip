@@ -151,8 +151,24 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(
     float* __restrict__ part_o, char* __restrict__ out) {
   constexpr int ES = DT == DT_BF16 ? 2 : 4;  // element size
   constexpr size_t kPageElems = (size_t)kPage * kHeadDim;
-  const int c = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int c = blockIdx.x, kvh = blockIdx.y;
   const int lane = threadIdx.x & 63;
+  // Longest sequences first: workgroups are dispatched in blockIdx order, so
+  // for up to 64 sequences blockIdx.z is read as a rank and mapped to the
+  // sequence with the rank-th largest kv_len (ties by index).  Each wave
+  // ranks the 64 lengths with one compare per lane and step.
+  int b = blockIdx.z;
+  const int batch = gridDim.z;
+  if (batch <= 64) {
+    const int li = lane < batch ? clampi(kv_lens[lane], 0, max_pages * kPage) : -1;
+    int rank = 0;
+    for (int j = 0; j < batch; ++j) {
+      const int lj = __builtin_amdgcn_readlane(li, j);
+      rank += (lj > li) || (lj == li && j < lane);
+    }
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(lane < batch && rank == (int)blockIdx.z);
+    b = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(hit));
+  }
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, g = lane >> 4;
   const int hq = hkv * group;
@@ -379,19 +395,22 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(
 // ============================================================= merge kernel
 //
 // CL*16 threads per (sequence, query head) row: thread (cl, dq) owns output
-// dims [4dq, 4dq+4) and the chunks c = cl, cl + CL, ...; partial o rows are
-// read with 16-byte loads (a chunk's 64 dims are 256 contiguous bytes).  The
-// chunk weights e^(m_c - M) and D = sum d_c e^(m_c - M) are formed by the
-// row's first wave; the CL partial sums of o are combined through LDS.
+// dims [4dq, 4dq+4) and the chunks c = cl, cl + CL, ...  Every thread issues
+// all its loads (m_c, d_c and the 16-byte slice of o_c) before using any, so
+// the merge costs one memory round trip; M, then the weights e^(m_c - M),
+// the partial sums of d and o, are combined across the CL chunk lanes
+// through LDS in a fixed order.
 
 template <int DT, int CL>
 __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pm,
                                                     const float* __restrict__ pd,
                                                     const float* __restrict__ po, int rows,
                                                     int splits, char* __restrict__ out) {
-  constexpr int TPR = 16 * CL;           // threads per row
-  constexpr int RPB = 256 / TPR;         // rows per block
-  __shared__ float sm_M[RPB], sm_D[RPB];
+  constexpr int TPR = 16 * CL;  // threads per row
+  constexpr int RPB = 256 / TPR;  // rows per block
+  constexpr int MAXC = 8;         // chunks held in registers per thread and pass
+  __shared__ float sm_m[RPB][CL];
+  __shared__ float sm_d[RPB][CL];
   __shared__ f32x4 sm_o[RPB][CL][16];
   const int t = threadIdx.x % TPR, rl = threadIdx.x / TPR;
   const int row = blockIdx.x * RPB + rl;
@@ -399,47 +418,60 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pm
   const bool live = row < rows;
   const float* m = pm + (size_t)row * splits;
   const float* d = pd + (size_t)row * splits;
-  // M and D by the first (up to 64) threads of the row
-  if (t < 64) {
-    float M = kNegInf, D = 0.f;
-    if (live) {
-      for (int c = t; c < splits; c += 64) M = fmaxf(M, m[c]);
-    }
-    const int lanes = TPR < 64 ? TPR : 64;
-    for (int k = 1; k < lanes; k <<= 1) M = fmaxf(M, __shfl_xor(M, k, lanes));
-    if (live) {
-      for (int c = t; c < splits; c += 64) {
-        const float mc = m[c];
-        D += (mc == kNegInf) ? 0.f : d[c] * fast_exp2((mc - M) * kLog2e);
-      }
-    }
-    for (int k = 1; k < lanes; k <<= 1) D += __shfl_xor(D, k, lanes);
-    if (t == 0) {
-      sm_M[rl] = M;
-      sm_D[rl] = D;
-    }
+  const float* o = po + (size_t)row * splits * kHeadDim + 4 * dq;
+
+  // The first CL*MAXC chunks (every workload here) are loaded once, all at
+  // the same time; chunks beyond that are read in a second, rarely used loop.
+  float mv[MAXC], dv[MAXC];
+  f32x4 ov[MAXC];
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    const int c = cl + i * CL;
+    const bool ok = live && c < splits;
+    mv[i] = ok ? m[c] : kNegInf;
+    dv[i] = ok ? d[c] : 0.f;
+    ov[i] = ok ? *reinterpret_cast<const f32x4*>(o + (size_t)c * kHeadDim)
+               : f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  float mloc = kNegInf;
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) mloc = fmaxf(mloc, mv[i]);
+  for (int c = cl + CL * MAXC; live && c < splits; c += CL) mloc = fmaxf(mloc, m[c]);
+  if (dq == 0) sm_m[rl][cl] = mloc;
   __syncthreads();
-  const float M = sm_M[rl];
+  float M = kNegInf;
+#pragma unroll
+  for (int k = 0; k < CL; ++k) M = fmaxf(M, sm_m[rl][k]);
+
+  float D = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  if (live) {
-    const float* o = po + (size_t)row * splits * kHeadDim + 4 * dq;
-    for (int c = cl; c < splits; c += CL) {
-      const float mc = m[c];
-      if (mc == kNegInf) continue;
-      acc += fast_exp2((mc - M) * kLog2e) * *reinterpret_cast<const f32x4*>(o + (size_t)c * kHeadDim);
-    }
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    const float e = (mv[i] == kNegInf) ? 0.f : fast_exp2((mv[i] - M) * kLog2e);
+    D += dv[i] * e;
+    acc += e * ov[i];
   }
+  for (int c = cl + CL * MAXC; live && c < splits; c += CL) {
+    const float mc = m[c];
+    if (mc == kNegInf) continue;
+    const float e = fast_exp2((mc - M) * kLog2e);
+    D += d[c] * e;
+    acc += e * *reinterpret_cast<const f32x4*>(o + (size_t)c * kHeadDim);
+  }
+  if (dq == 0) sm_d[rl][cl] = D;
   sm_o[rl][cl][dq] = acc;
   __syncthreads();
   if (cl == 0 && live) {
     f32x4 sum = sm_o[rl][0][dq];
+    float Dt = sm_d[rl][0];
 #pragma unroll
-    for (int k = 1; k < CL; ++k) sum += sm_o[rl][k][dq];
-    const float D = sm_D[rl];
+    for (int k = 1; k < CL; ++k) {
+      sum += sm_o[rl][k][dq];
+      Dt += sm_d[rl][k];
+    }
     float y[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) y[i] = D > 0.f ? sum[i] / D : 0.f;
+    for (int i = 0; i < 4; ++i) y[i] = Dt > 0.f ? sum[i] / Dt : 0.f;
     const size_t off = (size_t)row * kHeadDim + 4 * dq;
     if constexpr (DT == DT_BF16) {
       *reinterpret_cast<u32x2*>(out + off * 2) = u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
