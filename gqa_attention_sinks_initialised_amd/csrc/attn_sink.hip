@@ -675,25 +675,30 @@ prefill_kernel(const char* __restrict__ q, const char* __restrict__ k, const cha
 #pragma unroll
         for (int i = 0; i < 16; ++i) sacc[kb][rb][i] = 0.f;
 
-    // S^T = K Q^T
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int krw = kb * 32 + col;
-      const char* krow = kd + ((kb * 32 + col) * KROW + 32 * g) * ES;
+    // S^T = K Q^T.  bf16: k-step outermost so that the 2*RB accumulators
+    // are interleaved and consecutive MFMAs never depend on each other.
+    if constexpr (DT == DT_BF16) {
 #pragma unroll
       for (int s = 0; s < QV; ++s) {
-        u32x4 kf;
-        if constexpr (DT == DT_BF16)
-          kf = *reinterpret_cast<const u32x4*>(kd + krw * 128 + 16 * ((4 * g + s) ^ (krw & 7)));
-        else
-          kf = *reinterpret_cast<const u32x4*>(krow + 16 * s);
-        if constexpr (DT == DT_BF16) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const int krw = kb * 32 + col;
+          const u32x4 kf =
+              *reinterpret_cast<const u32x4*>(kd + krw * 128 + 16 * ((4 * g + s) ^ (krw & 7)));
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb)
             sacc[kb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                 __builtin_bit_cast(bf16x8, kf), __builtin_bit_cast(bf16x8, qf[rb][s]),
                 sacc[kb][rb], 0, 0, 0);
-        } else {
+        }
+      }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const char* krow = kd + ((kb * 32 + col) * KROW + 32 * g) * ES;
+#pragma unroll
+        for (int s = 0; s < QV; ++s) {
+          const u32x4 kf = *reinterpret_cast<const u32x4*>(krow + 16 * s);
 #pragma unroll
           for (int e = 0; e < 4; ++e)
 #pragma unroll
@@ -771,36 +776,45 @@ prefill_kernel(const char* __restrict__ q, const char* __restrict__ k, const cha
       d_run[rb] += (ps[0] + ps[1]) + (ps[2] + ps[3]);
     }
 
-    // O^T += V^T P^T
+    // O^T += V^T P^T.  bf16: key step outermost, both dim blocks' V^T
+    // operands read together, so the 2*RB accumulators interleave.
+    if constexpr (DT == DT_BF16) {
+      // source lane s of each 16-lane group points at V[kbase + s/4][dim0 +
+      // 4*(s%4)]; after the transposing read lane i holds V[kbase + 0..3]
+      // [dim0 + i] with dim0 + i = 32*db + lane%32
+      typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+      const int sl = lane & 15;
 #pragma unroll
-    for (int db = 0; db < 2; ++db) {
-      const char* vrow = vd + ((db * 32 + col) * VROW) * ES;
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        if constexpr (DT == DT_BF16) {
-          // source lane s of each 16-lane group points at V[kbase + s/4][dim0 +
-          // 4*(s%4)]; after the transposing read lane i holds V[kbase + 0..3]
-          // [dim0 + i] with dim0 + i = 32*db + lane%32
-          typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-          const int sl = lane & 15;
-          const int dim = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (sl & 3);
-          const int chunk = dim >> 3, sub = 2 * (dim & 7);
+        for (int hh = 0; hh < 2; ++hh) {
+          const int r0 = kb * 32 + 16 * hh + 4 * g + (sl >> 2), r1 = r0 + 8;
+          u32x4 vf[2];
 #pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const int r0 = kb * 32 + 16 * hh + 4 * g + (sl >> 2), r1 = r0 + 8;
+          for (int db = 0; db < 2; ++db) {
+            const int dim = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (sl & 3);
+            const int chunk = dim >> 3, sub = 2 * (dim & 7);
             const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (lds_i16x4*)(vd + r0 * 128 + 16 * (chunk ^ (2 * (r0 & 3))) + sub));
             const i16x4 c = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (lds_i16x4*)(vd + r1 * 128 + 16 * (chunk ^ (2 * (r1 & 3))) + sub));
             const u32x2 lo = __builtin_bit_cast(u32x2, a), hi = __builtin_bit_cast(u32x2, c);
-            const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
+            vf[db] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+          }
+#pragma unroll
+          for (int db = 0; db < 2; ++db)
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
               acc_o[db][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                  __builtin_bit_cast(bf16x8, vf), __builtin_bit_cast(bf16x8, pf[rb][kb][hh]),
+                  __builtin_bit_cast(bf16x8, vf[db]), __builtin_bit_cast(bf16x8, pf[rb][kb][hh]),
                   acc_o[db][rb], 0, 0, 0);
-          }
-        } else {
+        }
+    } else {
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+        const char* vrow = vd + ((db * 32 + col) * VROW) * ES;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int qd = 0; qd < 4; ++qd) {
             const u32x4 vf =
@@ -812,7 +826,6 @@ prefill_kernel(const char* __restrict__ q, const char* __restrict__ k, const cha
                 acc_o[db][rb] = __builtin_amdgcn_mfma_f32_32x32x2f32(
                     __uint_as_float(vf[e]), sacc[kb][rb][4 * qd + e], acc_o[db][rb], 0, 0, 0);
           }
-        }
       }
     }
   };
