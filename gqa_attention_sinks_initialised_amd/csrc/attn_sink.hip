@@ -38,6 +38,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 
 #include "attn_sink.h"
 
@@ -664,7 +666,7 @@ prefill_kernel(const char* __restrict__ q, const char* __restrict__ k, const cha
     }
   };
 
-  auto compute_tile = [&](int buf, int jt) {
+  auto compute_tile = [&](auto masked, int buf, int jt) {
     const char* kd = lds_k[buf];
     const char* vd = lds_v[buf];
     f32x16 sacc[2][RB];
@@ -714,18 +716,19 @@ prefill_kernel(const char* __restrict__ q, const char* __restrict__ k, const cha
     // and d are rescaled, in a wave-uniform, rarely taken branch); otherwise
     // p = 2^(x - m_run) stays below 2^kRescaleLog2.  O/d does not depend on
     // which reference is used.
-    const bool need_mask = (jt * BK + BK - 1) > lim_min;
     u32x4 pf[RB][2][2];  // bf16 P^T operands [rb][kb][half]
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      if (need_mask) {
+      if constexpr (decltype(masked)::value) {
+        // key = jt*BK + kb*32 + 4g + off(r) with off(r) = 8*(r/4) + r%4 a
+        // constant: compare off(r) with one per-lane threshold per key block
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb) {
+          const int thr = lim[rb] - (jt * BK + kb * 32 + 4 * g);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = jt * BK + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-            if (key > lim[rb]) sacc[kb][rb][r] = kNegInf;
-          }
+          for (int r = 0; r < 16; ++r)
+            sacc[kb][rb][r] = (8 * (r >> 2) + (r & 3) > thr) ? kNegInf : sacc[kb][rb][r];
+        }
       }
       float mx4[4] = {kNegInf, kNegInf, kNegInf, kNegInf};  // 4 chains of max3
 #pragma unroll
@@ -830,14 +833,26 @@ prefill_kernel(const char* __restrict__ q, const char* __restrict__ k, const cha
     }
   };
 
+  // Tiles below n_plain need no mask for any valid row of the workgroup; the
+  // remaining (diagonal / ragged-tail) tiles run the masked body.  Two loops
+  // keep the mask arithmetic out of the common path.
+  const int n_plain = min(n_tiles, max(0, (lim_min + 1) / BK));
   if (n_tiles > 0) {
     stage_load(0);
     stage_store(0);
     __syncthreads();
-    for (int jt = 0; jt < n_tiles; ++jt) {
+    int jt = 0;
+    for (; jt < n_plain; ++jt) {
       const bool more = jt + 1 < n_tiles;
       if (more) stage_load(jt + 1);
-      compute_tile(jt & 1, jt);
+      compute_tile(std::false_type{}, jt & 1, jt);
+      if (more) stage_store((jt + 1) & 1);
+      __syncthreads();
+    }
+    for (; jt < n_tiles; ++jt) {
+      const bool more = jt + 1 < n_tiles;
+      if (more) stage_load(jt + 1);
+      compute_tile(std::true_type{}, jt & 1, jt);
       if (more) stage_store((jt + 1) & 1);
       __syncthreads();
     }
