@@ -891,6 +891,12 @@ int launch_status() {
   return hipGetLastError() == hipSuccess ? ATTN_SINK_OK : ATTN_SINK_ERR_LAUNCH;
 }
 
+// bf16 prefill: waves of 64 rows per workgroup.
+#ifndef ATTN_SINK_PREFILL_WAVES
+#define ATTN_SINK_PREFILL_WAVES 4
+#endif
+constexpr int kPrefillWaves = ATTN_SINK_PREFILL_WAVES;
+
 // Decode workgroup shape: waves per workgroup and pages per register group
 // (two groups are in flight per wave).
 #ifndef ATTN_SINK_DECODE_WAVES
@@ -944,7 +950,8 @@ int attn_sink_prefill(const void* q, const void* k, const void* v, const float* 
   const float qk = sm_scale * kLog2e;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int n_pairs = batch * num_kv_heads;
-  const int tb = 4 * (64 / group_size);  // 4 waves of 64 rows
+  const int waves = dtype == ATTN_SINK_BF16 ? kPrefillWaves : 4;
+  const int tb = waves * (64 / group_size);  // waves of 64 rows
   const int n_qtiles = (max_seqlen_q + tb - 1) / tb;
   if ((int64_t)n_qtiles * n_pairs > INT32_MAX) return ATTN_SINK_ERR_UNSUPPORTED;
   const dim3 grid(n_qtiles * n_pairs);
@@ -954,7 +961,8 @@ int attn_sink_prefill(const void* q, const void* k, const void* v, const float* 
                        total_q, total_kv, num_kv_heads, group_size, qk, causal, n_qtiles,
                        n_pairs, (char*)out);
   else
-    hipLaunchKernelGGL((prefill_kernel<DT_BF16, 2, 4>), grid, dim3(256), 0, s, (const char*)q,
+    hipLaunchKernelGGL((prefill_kernel<DT_BF16, 2, kPrefillWaves>), grid, dim3(64 * kPrefillWaves),
+                       0, s, (const char*)q,
                        (const char*)k, (const char*)v, sinks, cu_seqlens_q, cu_seqlens_kv,
                        total_q, total_kv, num_kv_heads, group_size, qk, causal, n_qtiles,
                        n_pairs, (char*)out);
