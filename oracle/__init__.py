@@ -55,10 +55,17 @@ def _load():
         lib.oracle_decode_partials_rows.argtypes = [P, P, P, I, P, P, P, I, I, I, I,
                                                     I, I, D, I, I, L, P, P, P, P, P,
                                                     P]
+        lib.oracle_prefill_partials_rows.argtypes = [P, P, P, I, P, P, P, I, I, I,
+                                                     I, D, I, I, I, I, L, P, P, P,
+                                                     P, P, P]
+        lib.oracle_prefill_paged_rows.argtypes = [P, P, P, I, P, P, P, P, I, I, I,
+                                                  I, I, I, D, I, I, I, L, P, P, P,
+                                                  P, P, P, P]
         lib.oracle_merge.argtypes = [P, P, P, L, I, I, P]
         lib.oracle_max_threads.argtypes = []
         for f in (lib.oracle_prefill_rows, lib.oracle_decode_paged_rows,
-                  lib.oracle_decode_partials_rows, lib.oracle_merge,
+                  lib.oracle_decode_partials_rows, lib.oracle_prefill_partials_rows,
+                  lib.oracle_prefill_paged_rows, lib.oracle_merge,
                   lib.oracle_max_threads):
             f.restype = ctypes.c_int
         _lib = lib
@@ -154,6 +161,97 @@ def prefill(q, k, v, sinks, cu_q, cu_kv, num_kv_heads: int, group: int,
     if rows is None:
         return out.reshape(total_q, hq, dim)
     return out
+
+
+def _prefill_rows(total_q, hq, rows):
+    if rows is None:
+        toks = np.repeat(np.arange(total_q, dtype=np.int64), hq)
+        heads = np.tile(np.arange(hq, dtype=np.int32), total_q)
+    else:
+        toks = np.ascontiguousarray(np.asarray(rows[0], dtype=np.int64))
+        heads = np.ascontiguousarray(np.asarray(rows[1], dtype=np.int32))
+    return toks, heads
+
+
+def prefill_partials(q, k, v, sinks, cu_q, cu_kv, num_kv_heads: int, group: int,
+                     sm_scale: float, causal: bool, splits: int, unit: int = 16,
+                     rows=None):
+    """Split-KV partial states of ragged prefill; each sequence's keys are cut
+    into S chunks of ceil(ceil(Lkv/unit)/S) units and only chunk 0 carries
+    the sink.  Returns m, d [..., S] and o [..., S, D] with ... = [total_q, Hq]
+    for rows=None, else [n_rows]."""
+    qa, dt = _elems(q)
+    ka, dk = _elems(k)
+    va, dv = _elems(v)
+    if not (dt == dk == dv):
+        raise TypeError("q, k, v must share one element type")
+    cq, ck = _i32(cu_q), _i32(cu_kv)
+    s = _f64(sinks)
+    total_q, hq, dim = qa.shape
+    if hq != num_kv_heads * group:
+        raise ValueError("q heads != num_kv_heads * group")
+    batch = len(cq) - 1
+    toks, heads = _prefill_rows(total_q, hq, rows)
+    n = len(toks)
+    max_kv = int(max(1, (ck[1:] - ck[:-1]).max() if batch > 0 else 1))
+    m = np.zeros((n, splits), dtype=np.float64)
+    d = np.zeros((n, splits), dtype=np.float64)
+    o = np.zeros((n, splits, dim), dtype=np.float64)
+    scratch = np.zeros(max_threads() * max_kv, dtype=np.float64)
+    rc = _load().oracle_prefill_partials_rows(
+        _ptr(qa), _ptr(ka), _ptr(va), dt, _ptr(s), _ptr(cq), _ptr(ck), batch,
+        num_kv_heads, group, dim, float(sm_scale), int(bool(causal)), int(unit),
+        int(splits), max_kv, n, _ptr(toks), _ptr(heads), _ptr(m), _ptr(d), _ptr(o),
+        _ptr(scratch))
+    if rc != 0:
+        raise ValueError("oracle_prefill_partials_rows: bad row")
+    if rows is None:
+        return (m.reshape(total_q, hq, splits), d.reshape(total_q, hq, splits),
+                o.reshape(total_q, hq, splits, dim))
+    return m, d, o
+
+
+def prefill_paged(q, k_cache, v_cache, page_table, cu_q, kv_lens, sinks, group: int,
+                  sm_scale: float, causal: bool, splits: int = 0, rows=None):
+    """Paged (chunked) prefill.  q [total_q, Hkv*G, D]; k_cache [pages, Hkv, P, D];
+    v_cache [pages, Hkv, D, P]; page_table [B, max_pages]; cu_q [B+1];
+    kv_lens [B] (all keys in the cache, the new tokens' included).
+
+    splits=0 returns the attention output ([total_q, Hq, D] or [n_rows, D]);
+    splits>=1 returns the partial states (m, d, o) of page-aligned chunks."""
+    qa, dt = _elems(q)
+    ka, dk = _elems(k_cache)
+    va, dv = _elems(v_cache)
+    if not (dt == dk == dv):
+        raise TypeError("q, k_cache, v_cache must share one element type")
+    pt, cq, lens, s = _i32(page_table), _i32(cu_q), _i32(kv_lens), _f64(sinks)
+    total_q, hq, dim = qa.shape
+    hkv, psz = ka.shape[1], ka.shape[2]
+    if hq != hkv * group:
+        raise ValueError("q heads != num_kv_heads * group")
+    batch = len(cq) - 1
+    toks, heads = _prefill_rows(total_q, hq, rows)
+    n = len(toks)
+    max_len = int(max(1, lens.max() if batch > 0 else 1))
+    S = int(splits)
+    out = np.zeros((n, dim), dtype=np.float64)
+    m = np.zeros((n, max(S, 1)), dtype=np.float64)
+    d = np.zeros((n, max(S, 1)), dtype=np.float64)
+    o = np.zeros((n, max(S, 1), dim), dtype=np.float64)
+    scratch = np.zeros(max_threads() * max_len, dtype=np.float64)
+    rc = _load().oracle_prefill_paged_rows(
+        _ptr(qa), _ptr(ka), _ptr(va), dt, _ptr(pt), _ptr(cq), _ptr(lens), _ptr(s),
+        batch, pt.shape[1], hkv, group, dim, psz, float(sm_scale),
+        int(bool(causal)), S, max_len, n, _ptr(toks), _ptr(heads), _ptr(out),
+        _ptr(m), _ptr(d), _ptr(o), _ptr(scratch))
+    if rc != 0:
+        raise ValueError("oracle_prefill_paged_rows: bad row")
+    if S == 0:
+        return out.reshape(total_q, hq, dim) if rows is None else out
+    if rows is None:
+        return (m.reshape(total_q, hq, S), d.reshape(total_q, hq, S),
+                o.reshape(total_q, hq, S, dim))
+    return m, d, o
 
 
 def _decode_rows(q, rows):

@@ -55,7 +55,13 @@
  *     splits, ppc = ceil(np/S) pages per chunk, chunk c covers tokens
  *     [c*ppc*P, min((c+1)*ppc*P, L)).  An empty chunk c > 0 has state
  *     (-inf, 0, 0); an empty chunk 0 has (s, 1, 0) (or (-inf, 0, 0) when
- *     s = -inf).
+ *     s = -inf).  Split prefill cuts each sequence's key range by the same
+ *     rule (16-key units when the keys are not paged); a row's chunk then
+ *     holds only the keys of the chunk that the row can see;
+ *   - paged prefill (several new query tokens per sequence against the
+ *     cache): kv_lens[b] counts every key in the cache, the new tokens'
+ *     included, and the Lq queries are the last Lq positions, which the
+ *     bottom-right causal rule above expresses.
  *
  * Element types accepted for inputs: 0 = fp32, 1 = bf16 (raw 16-bit
  * patterns, widened exactly to fp32 then fp64), 2 = fp64.  Outputs are fp64.
@@ -119,6 +125,68 @@ static void sink_softmax_row(int n, const double *x, double sink, int dim,
     }
 }
 
+/*
+ * State (m, d, o) of the keys [t0, t1) of one row (logits x), the block
+ * representation of the split along the key length: m = max of the block's
+ * logits, and of the sink when the block carries it; d = sum of exp(z - m)
+ * over the block's logits (and the sink); o = sum of exp(x_j - m) * v_j.
+ * A block with nothing in it (no key, and no finite sink) is (-inf, 0, 0).
+ */
+static void block_state(const double *x, int64_t t0, int64_t t1, int with_sink,
+                        double sink, int dim, value_fn vrow, const void *ctx,
+                        double *m_out, double *d_out, double *o)
+{
+    double m = with_sink ? sink : -INFINITY;
+    for (int64_t t = t0; t < t1; ++t)
+        if (x[t] > m)
+            m = x[t];
+    for (int d = 0; d < dim; ++d)
+        o[d] = 0.0;
+    double den = 0.0;
+    if (m != -INFINITY) {
+        if (with_sink)
+            den = exp(sink - m);
+        for (int64_t t = t0; t < t1; ++t) {
+            double e = exp(x[t] - m);
+            den += e;
+            for (int d = 0; d < dim; ++d)
+                o[d] += e * vrow(ctx, (int)t, d);
+        }
+    }
+    *m_out = m;
+    *d_out = den;
+}
+
+/* Chunk c of S over a key range of length L, in units of `unit` tokens:
+ * ppc = ceil(ceil(L / unit) / S) units per chunk; [t0, t1) clipped to L. */
+static void chunk_range(int64_t L, int unit, int splits, int c, int64_t *t0,
+                        int64_t *t1)
+{
+    const int64_t nu = (L + unit - 1) / unit;
+    const int64_t ppc = (nu + splits - 1) / splits;
+    int64_t a = (int64_t)c * ppc * unit, e = a + ppc * unit;
+    *t0 = a > L ? L : a;
+    *t1 = e > L ? L : e;
+}
+
+/* Sequence holding packed query token tok (cu_q prefix offsets), or -1. */
+static int seq_of(const int32_t *cu_q, int batch, int64_t tok)
+{
+    for (int i = 0; i < batch; ++i)
+        if (tok >= cu_q[i] && tok < cu_q[i + 1])
+            return i;
+    return -1;
+}
+
+/* Keys visible to row i of a sequence with lq queries and lkv keys. */
+static int64_t visible_keys(int64_t i, int64_t lq, int64_t lkv, int causal)
+{
+    if (!causal)
+        return lkv;
+    int64_t n = i + (lkv - lq) + 1;          /* bottom-right alignment */
+    return n < 0 ? 0 : (n > lkv ? lkv : n);
+}
+
 /* ---------------------------------------------------------------- prefill */
 
 struct ragged_v {
@@ -143,28 +211,14 @@ static int prefill_one(const void *q, const void *k, const void *v, int dt,
                        int dim, double scale, int causal, int64_t tok, int h,
                        double *x, double *out)
 {
-    int b = -1;
-    for (int i = 0; i < batch; ++i)
-        if (tok >= cu_q[i] && tok < cu_q[i + 1]) {
-            b = i;
-            break;
-        }
+    const int b = seq_of(cu_q, batch, tok);
     if (b < 0)
         return -1;
     const int hq = hkv * group;
     const int g = h / group;                 /* GQA: query head -> kv head */
     const int64_t lq = cu_q[b + 1] - cu_q[b];
     const int64_t lkv = cu_kv[b + 1] - cu_kv[b];
-    const int64_t i = tok - cu_q[b];
-    int64_t n = lkv;
-    if (causal) {
-        int64_t last = i + (lkv - lq);       /* bottom-right alignment */
-        n = last + 1;
-        if (n > lkv)
-            n = lkv;
-        if (n < 0)
-            n = 0;
-    }
+    const int64_t n = visible_keys(tok - cu_q[b], lq, lkv, causal);
     for (int64_t j = 0; j < n; ++j) {
         double acc = 0.0;
         for (int d = 0; d < dim; ++d)
@@ -314,38 +368,140 @@ int oracle_decode_partials_rows(const void *q, const void *kc, const void *vc,
         for (int64_t t = 0; t < L; ++t)
             x[t] = paged_logit(q, kc, dt, pages, t, qoff, g, hkv, dim, psz,
                                scale);
-        /* page-aligned chunks: ppc = ceil(ceil(L/P) / S) pages each */
-        const int64_t np = (L + psz - 1) / psz;
-        const int64_t ppc = (np + splits - 1) / splits;
+        /* page-aligned chunks: ppc = ceil(ceil(L/P) / S) pages each; only
+         * chunk 0 carries the sink */
         struct paged_v ctx = {vc, dt, pages, 0, hkv, g, dim, psz};
         for (int c = 0; c < splits; ++c) {
-            int64_t t0 = (int64_t)c * ppc * psz;
-            int64_t t1 = t0 + ppc * psz;
-            if (t0 > L)
-                t0 = L;
-            if (t1 > L)
-                t1 = L;
+            int64_t t0, t1;
+            chunk_range(L, psz, splits, c, &t0, &t1);
             const int64_t st = r * splits + c;
-            double *o = o_out + st * dim;
-            double m = (c == 0) ? sinks[h] : -INFINITY;
-            for (int64_t t = t0; t < t1; ++t)
-                if (x[t] > m)
-                    m = x[t];
+            block_state(x, t0, t1, c == 0, sinks[h], dim, paged_v_at, &ctx,
+                        m_out + st, d_out + st, o_out + st * dim);
+        }
+    }
+    return bad ? -1 : 0;
+}
+
+/* ------------------------------------------------- split prefill, paged prefill */
+
+/*
+ * Split-KV partial states of ragged prefill for selected (token, head) rows.
+ * The key range of each sequence is cut by the chunk rule above (units of
+ * `unit` keys, ppc = ceil(ceil(Lkv / unit) / S)); a row's chunk c holds the
+ * chunk's keys that the row can see, and only chunk 0 carries the sink.
+ * Layouts as in oracle_prefill_rows; m, d [n_rows, S], o [n_rows, S, D].
+ */
+int oracle_prefill_partials_rows(const void *q, const void *k, const void *v,
+                                 int dt, const double *sinks,
+                                 const int32_t *cu_q, const int32_t *cu_kv,
+                                 int batch, int hkv, int group, int dim,
+                                 double scale, int causal, int unit, int splits,
+                                 int max_kv, int64_t n_rows,
+                                 const int64_t *row_tok, const int32_t *row_head,
+                                 double *m_out, double *d_out, double *o_out,
+                                 double *scratch)
+{
+    const int hq = hkv * group;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 4) reduction(| : bad)
+    for (int64_t r = 0; r < n_rows; ++r) {
+        const int64_t tok = row_tok[r];
+        const int h = row_head[r];
+        const int b = seq_of(cu_q, batch, tok);
+        if (b < 0 || h < 0 || h >= hq) {
+            bad = 1;
+            continue;
+        }
+        double *x = scratch + (int64_t)thread_id() * (max_kv > 0 ? max_kv : 1);
+        const int g = h / group;
+        const int64_t lkv = cu_kv[b + 1] - cu_kv[b];
+        const int64_t n = visible_keys(tok - cu_q[b], cu_q[b + 1] - cu_q[b], lkv,
+                                       causal);
+        for (int64_t j = 0; j < n; ++j) {
+            double acc = 0.0;
             for (int d = 0; d < dim; ++d)
-                o[d] = 0.0;
-            double den = 0.0;
-            if (m != -INFINITY) {
-                if (c == 0)
-                    den = exp(sinks[h] - m);
-                for (int64_t t = t0; t < t1; ++t) {
-                    double e = exp(x[t] - m);
-                    den += e;
-                    for (int d = 0; d < dim; ++d)
-                        o[d] += e * paged_v_at(&ctx, (int)t, d);
-                }
-            }
-            m_out[st] = m;
-            d_out[st] = den;
+                acc += elem(q, dt, (tok * hq + h) * (int64_t)dim + d) *
+                       elem(k, dt, ((cu_kv[b] + j) * hkv + g) * (int64_t)dim + d);
+            x[j] = scale * acc;
+        }
+        struct ragged_v ctx = {v, dt, cu_kv[b], (int64_t)hkv * dim,
+                               (int64_t)g * dim};
+        for (int c = 0; c < splits; ++c) {
+            int64_t t0, t1;
+            chunk_range(lkv, unit, splits, c, &t0, &t1);
+            if (t1 > n)
+                t1 = n;             /* keys past the row's causal limit */
+            if (t0 > t1)
+                t0 = t1;
+            const int64_t st = r * splits + c;
+            block_state(x, t0, t1, c == 0, sinks[h], dim, ragged_v_at, &ctx,
+                        m_out + st, d_out + st, o_out + st * dim);
+        }
+    }
+    return bad ? -1 : 0;
+}
+
+/*
+ * Paged prefill: several query tokens per sequence against the paged cache
+ * (chunked prefill; "Fast embeddings on GPUs", section "ROSE").  Sequence b
+ * has Lq = cu_q[b+1] - cu_q[b] query tokens and Lkv = kv_lens[b] keys in the
+ * cache, the queries being the last Lq positions for the causal mask.
+ *   q [total_q, Hkv*G, D]; k_cache [num_pages, Hkv, P, D];
+ *   v_cache [num_pages, Hkv, D, P]; page_table [batch, max_pages].
+ * splits == 0: full result into out [n_rows, D].  splits >= 1: partial
+ * states into m, d [n_rows, S] and o [n_rows, S, D], chunks of whole pages
+ * as in oracle_decode_partials_rows, clipped to each row's visible keys.
+ *   scratch: oracle_max_threads() * max_len doubles.
+ */
+int oracle_prefill_paged_rows(const void *q, const void *kc, const void *vc,
+                              int dt, const int32_t *page_table,
+                              const int32_t *cu_q, const int32_t *kv_lens,
+                              const double *sinks, int batch, int max_pages,
+                              int hkv, int group, int dim, int psz, double scale,
+                              int causal, int splits, int max_len,
+                              int64_t n_rows, const int64_t *row_tok,
+                              const int32_t *row_head, double *out,
+                              double *m_out, double *d_out, double *o_out,
+                              double *scratch)
+{
+    const int hq = hkv * group;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 4) reduction(| : bad)
+    for (int64_t r = 0; r < n_rows; ++r) {
+        const int64_t tok = row_tok[r];
+        const int h = row_head[r];
+        const int b = seq_of(cu_q, batch, tok);
+        if (b < 0 || h < 0 || h >= hq || kv_lens[b] > max_len ||
+            kv_lens[b] > (int64_t)max_pages * psz) {
+            bad = 1;
+            continue;
+        }
+        double *x = scratch + (int64_t)thread_id() * (max_len > 0 ? max_len : 1);
+        const int32_t *pages = page_table + (int64_t)b * max_pages;
+        const int g = h / group;
+        const int64_t lkv = kv_lens[b];
+        const int64_t n = visible_keys(tok - cu_q[b], cu_q[b + 1] - cu_q[b], lkv,
+                                       causal);
+        const int64_t qoff = (tok * hq + h) * (int64_t)dim;
+        for (int64_t t = 0; t < n; ++t)
+            x[t] = paged_logit(q, kc, dt, pages, t, qoff, g, hkv, dim, psz,
+                               scale);
+        struct paged_v ctx = {vc, dt, pages, 0, hkv, g, dim, psz};
+        if (splits == 0) {
+            sink_softmax_row((int)n, x, sinks[h], dim, paged_v_at, &ctx,
+                             out + r * (int64_t)dim);
+            continue;
+        }
+        for (int c = 0; c < splits; ++c) {
+            int64_t t0, t1;
+            chunk_range(lkv, psz, splits, c, &t0, &t1);
+            if (t1 > n)
+                t1 = n;
+            if (t0 > t1)
+                t0 = t1;
+            const int64_t st = r * splits + c;
+            block_state(x, t0, t1, c == 0, sinks[h], dim, paged_v_at, &ctx,
+                        m_out + st, d_out + st, o_out + st * dim);
         }
     }
     return bad ? -1 : 0;

@@ -382,3 +382,137 @@ def test_sampled_rows_match_full():
                         p["cu_seqlens_kv"], 2, 2, 0.5, True, rows=([0, 15, 8], [3, 0, 2]))
     for r, (t, h) in enumerate(zip([0, 15, 8], [3, 0, 2])):
         np.testing.assert_array_equal(pr[r], pf[t, h])
+
+
+# ------------------------------------------------- O9: paged (chunked) prefill
+def _paged_prefill_case(lens_q, lens_kv, hq=8, hkv=2, dim=16, seed=0, fill=float("nan")):
+    d = workloads.prefill_inputs(lens_q, lens_kv, hq=hq, hkv=hkv, dim=dim,
+                                 dtype=torch.float32, seed=seed, sink_std=1.5)
+    d.update(workloads.pack_paged(d["k"], d["v"], d["lens_kv"], seed=seed + 1,
+                                  extra_pages=3, fill=fill))
+    return d
+
+
+@pytest.mark.parametrize("lens_q,lens_kv,causal", [
+    ([5, 20, 1], [37, 20, 64], True),      # new tokens at the end of a longer cache
+    ([5, 20, 1], [37, 20, 64], False),
+    ([9, 3], [4, 0], True),                # more queries than keys; an empty cache
+    ([16, 17], [16, 33], True)])           # page-boundary lengths
+def test_paged_prefill_equals_ragged_prefill_bitwise(lens_q, lens_kv, causal):
+    """The paged oracle on a cache scattered by pack_paged (random placement,
+    NaN in every slot no key owns) reads the same values in the same order as
+    the ragged oracle on the contiguous k / v, so the fp64 results are equal
+    bit for bit; a wrong page index, slot, or V-page orientation breaks it."""
+    d = _paged_prefill_case(lens_q, lens_kv, seed=len(lens_q) + int(causal))
+    ref = oracle.prefill(d["q"], d["k"], d["v"], d["sinks"], d["cu_seqlens_q"],
+                         d["cu_seqlens_kv"], 2, 4, 0.3, causal)
+    got = oracle.prefill_paged(d["q"], d["k_cache"], d["v_cache"], d["page_table"],
+                               d["cu_seqlens_q"], d["kv_lens"], d["sinks"], 4, 0.3, causal)
+    assert np.all(np.isfinite(got))
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_paged_prefill_single_query_equals_decode():
+    """One query token per sequence with the causal rule is exactly decode."""
+    d = _paged_prefill_case([1, 1, 1, 1], [1, 16, 40, 129], seed=11)
+    pre = oracle.prefill_paged(d["q"], d["k_cache"], d["v_cache"], d["page_table"],
+                               d["cu_seqlens_q"], d["kv_lens"], d["sinks"], 4, 0.25, True)
+    dec = oracle.decode_paged(d["q"], d["k_cache"], d["v_cache"], d["page_table"],
+                              d["kv_lens"], d["sinks"], 4, 0.25)
+    np.testing.assert_array_equal(pre, dec)
+
+
+@pytest.mark.parametrize("lq,lkv", [(6, 40), (40, 40), (50, 40), (1, 64)])
+def test_paged_prefill_bottom_right_causal_closed_form(lq, lkv):
+    """q = 0 makes every logit 0; one-hot values v_j = e_j then give
+    out[i, d] = 1 / (n_i + e^s) for d < n_i and 0 beyond, where n_i =
+    clip(i + lkv - lq + 1, 0, lkv) counts the keys row i sees (the queries
+    are the last lq positions)."""
+    dim = 64
+    d = _paged_prefill_case([lq], [lkv], hq=2, hkv=1, dim=dim, seed=lq)
+    q0 = torch.zeros_like(d["q"])
+    v1 = torch.zeros((lkv, 1, dim))
+    v1[torch.arange(lkv), 0, torch.arange(lkv)] = 1.0
+    pk = workloads.pack_paged(d["k"], v1, [lkv], seed=5, fill=float("nan"))
+    sinks = torch.tensor([0.7, -math.inf])
+    got = oracle.prefill_paged(q0, pk["k_cache"], pk["v_cache"], pk["page_table"],
+                               d["cu_seqlens_q"], pk["kv_lens"], sinks, 2, 0.125, True)
+    for i in range(lq):
+        n = min(max(i + lkv - lq + 1, 0), lkv)
+        for h in range(2):
+            s = float(sinks[h])                 # the fp32 value the oracle reads
+            want = np.zeros(dim)
+            if n > 0:
+                want[:n] = 1.0 / (n + math.exp(s))
+            np.testing.assert_allclose(got[i, h], want, rtol=1e-15, atol=0)
+
+
+# ------------------------------------------------------ O10: split-KV prefill
+@pytest.mark.parametrize("splits", [1, 2, 3, 7, 64])
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_split_merge_equals_unsplit(splits, causal):
+    """Merging the split prefill states gives the unsplit result, for the
+    ragged and the paged layout alike."""
+    d = _paged_prefill_case([3, 30, 1, 0], [85, 30, 17, 5], seed=splits)
+    ref = oracle.prefill(d["q"], d["k"], d["v"], d["sinks"], d["cu_seqlens_q"],
+                         d["cu_seqlens_kv"], 2, 4, 0.3, causal)
+    parts = oracle.prefill_partials(d["q"], d["k"], d["v"], d["sinks"], d["cu_seqlens_q"],
+                                    d["cu_seqlens_kv"], 2, 4, 0.3, causal, splits)
+    np.testing.assert_allclose(oracle.merge(*parts), ref, rtol=1e-12, atol=1e-13)
+    pp = oracle.prefill_paged(d["q"], d["k_cache"], d["v_cache"], d["page_table"],
+                              d["cu_seqlens_q"], d["kv_lens"], d["sinks"], 4, 0.3, causal,
+                              splits=splits)
+    for a, b in zip(pp, parts):
+        np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_prefill_split_bookkeeping_causal_rows(paged):
+    """Chunks follow the sequence's key range (85 keys, 6 units of 16, S = 4
+    -> 32 keys per chunk) and are clipped to each row's causal limit: rows
+    0..2 of 3 new tokens see 83, 84, 85 keys, so chunk 2 holds 19, 20, 21
+    keys and chunk 3 none.  q = 0 and unit values make d and o count keys;
+    the sink (0.5) sits in chunk 0 only."""
+    d = _paged_prefill_case([3], [85], hq=2, hkv=1, dim=4, seed=3)
+    q0 = torch.zeros_like(d["q"])
+    v1 = torch.ones_like(d["v"])
+    sinks = torch.tensor([-math.inf, 0.5])
+    if paged:
+        pk = workloads.pack_paged(d["k"], v1, [85], seed=8, fill=float("nan"))
+        m, dd, o = oracle.prefill_paged(q0, pk["k_cache"], pk["v_cache"], pk["page_table"],
+                                        d["cu_seqlens_q"], pk["kv_lens"], sinks, 2, 0.3,
+                                        True, splits=4)
+    else:
+        m, dd, o = oracle.prefill_partials(q0, d["k"], v1, sinks, d["cu_seqlens_q"],
+                                           d["cu_seqlens_kv"], 1, 2, 0.3, True, 4)
+    expect = {0: [32, 32, 19, 0], 1: [32, 32, 20, 0], 2: [32, 32, 21, 0]}
+    for i, counts in expect.items():
+        for c, n in enumerate(counts):
+            if n == 0:
+                assert m[i, 0, c] == -math.inf and dd[i, 0, c] == 0.0
+                assert m[i, 1, c] == -math.inf and dd[i, 1, c] == 0.0
+                assert np.all(o[i, :, c] == 0.0)
+                continue
+            assert m[i, 0, c] == 0.0 and dd[i, 0, c] == n
+            np.testing.assert_array_equal(o[i, 0, c], np.full(4, float(n)))
+            if c == 0:
+                assert m[i, 1, 0] == 0.5
+                assert dd[i, 1, 0] == pytest.approx(1.0 + n * math.exp(-0.5), rel=1e-15)
+                np.testing.assert_allclose(o[i, 1, 0], n * math.exp(-0.5), rtol=1e-15)
+            else:
+                assert m[i, 1, c] == 0.0 and dd[i, 1, c] == n
+
+
+def test_prefill_split_empty_rows_keep_sink_in_chunk_zero():
+    """A row that sees no key (more queries than keys) has (s, 1, 0) in
+    chunk 0 and (-inf, 0, 0) elsewhere."""
+    d = _paged_prefill_case([6], [2], hq=2, hkv=1, dim=4, seed=2)
+    sinks = torch.tensor([1.25, -math.inf])
+    m, dd, o = oracle.prefill_partials(d["q"], d["k"], d["v"], sinks, d["cu_seqlens_q"],
+                                       d["cu_seqlens_kv"], 1, 2, 0.3, True, 3)
+    for i in range(4):                       # rows 0..3 see 0 keys
+        assert m[i, 0, 0] == 1.25 and dd[i, 0, 0] == 1.0 and np.all(o[i, 0, 0] == 0)
+        assert m[i, 1, 0] == -math.inf and dd[i, 1, 0] == 0.0
+        for c in (1, 2):
+            assert m[i, :, c].tolist() == [-math.inf, -math.inf]
+            assert np.all(dd[i, :, c] == 0) and np.all(o[i, :, c] == 0)

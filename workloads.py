@@ -12,6 +12,8 @@ Layouts (shared by every caller):
                    v_cache [num_pages, Hkv, D, P] (dim-major pages),
                    page_table [B, max_pages] int32 (-1 past a sequence's last
                    page), kv_lens [B] int32, sinks [Hq] fp32
+  paged prefill:   q [total_q, Hq, D] with cu_seqlens_q, and the paged cache
+                   of decode (pack_paged lays ragged k / v out that way)
 
 The five named workloads follow the benchmark configurations of the project:
   1  tiny causal prefill, fp32: B=1, L=128, Hq=8, Hkv=2, D=64
@@ -98,6 +100,33 @@ def page_table_for(kv_lens, page=PAGE, seed=0, max_pages=None, pad=-1,
         pt[b, :n] = perm[off:off + n]
         off += n
     return pt, num_pages
+
+
+def pack_paged(k, v, lens_kv, page=PAGE, seed=0, max_pages=None, extra_pages=0,
+               fill=0.0):
+    """Scatter ragged k / v [total_kv, Hkv, D] into a paged cache: K pages
+    [num_pages, Hkv, P, D], V pages [num_pages, Hkv, D, P] (dim-major), with
+    the random placement of page_table_for.  Slots past a sequence's last key
+    and pages no sequence uses hold `fill` (e.g. NaN, to show they are never
+    read).  Returns dict(k_cache, v_cache, page_table, kv_lens, num_pages,
+    max_pages) on k's device."""
+    lens = [int(x) for x in lens_kv]
+    pt, num_pages = page_table_for(lens, page, seed, max_pages, extra_pages=extra_pages)
+    total, hkv, dim = k.shape
+    dev = k.device
+    kc = torch.full((num_pages, hkv, page, dim), fill, dtype=k.dtype, device=dev)
+    vc = torch.full((num_pages, hkv, dim, page), fill, dtype=v.dtype, device=dev)
+    if total > 0:
+        lt = torch.as_tensor(lens, dtype=torch.int64)
+        seq = torch.repeat_interleave(torch.arange(len(lens)), lt)
+        pos = torch.arange(total) - cu_from_lens(lens).long()[seq]
+        phys = pt.long()[seq, pos // page].to(dev)
+        slot = (pos % page).to(dev)
+        kc[phys, :, slot, :] = k            # token t -> page row t % P
+        vc[phys, :, :, slot] = v            # token t -> page column t % P
+    return dict(k_cache=kc, v_cache=vc, page_table=pt.to(dev),
+                kv_lens=torch.as_tensor(lens, dtype=torch.int32).to(dev),
+                num_pages=num_pages, max_pages=pt.shape[1])
 
 
 def decode_inputs(kv_lens, *, hq=8, hkv=2, dim=HEAD_DIM, page=PAGE,
