@@ -27,8 +27,8 @@ PAGE_SIZE = 16
 
 _lib = None
 
-SYMBOLS = ("attn_sink_prefill", "attn_sink_decode_paged", "attn_sink_merge",
-           "attn_sink_status_string")
+SYMBOLS = ("attn_sink_prefill", "attn_sink_prefill_partials", "attn_sink_prefill_paged",
+           "attn_sink_decode_paged", "attn_sink_merge", "attn_sink_status_string")
 
 
 class AttnSinkError(RuntimeError):
@@ -48,8 +48,13 @@ def load_library(path: str = LIB_PATH):
     lib.attn_sink_prefill.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, I, P, P]
     lib.attn_sink_decode_paged.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, I,
                                            P, P, P, P, P]
+    lib.attn_sink_prefill_partials.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, F, I,
+                                               I, I, P, P, P, P]
+    lib.attn_sink_prefill_paged.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I,
+                                            F, I, I, I, P, P, P, P, P]
     lib.attn_sink_merge.argtypes = [P, P, P, I, I, I, I, I, P, P]
-    for f in (lib.attn_sink_prefill, lib.attn_sink_decode_paged, lib.attn_sink_merge):
+    for f in (lib.attn_sink_prefill, lib.attn_sink_prefill_partials,
+              lib.attn_sink_prefill_paged, lib.attn_sink_decode_paged, lib.attn_sink_merge):
         f.restype = ctypes.c_int
     lib.attn_sink_status_string.argtypes = [I]
     lib.attn_sink_status_string.restype = ctypes.c_char_p
@@ -129,6 +134,100 @@ def attn_sink_prefill(q, k, v, sinks, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q:
         float(sm_scale), int(bool(causal)), dt, _ptr(out), _stream(stream))
     _check(rc, "attn_sink_prefill")
     return out
+
+
+def _partials(q, S, partial_m, partial_d, partial_o):
+    """Allocate missing split partial buffers [rows, Hq, S] / [rows, Hq, S, D]."""
+    import torch
+    rows, hq, dim = q.shape
+    f32 = dict(device=q.device, dtype=torch.float32)
+    if partial_m is None:
+        partial_m = torch.empty((rows, hq, S), **f32)
+    if partial_d is None:
+        partial_d = torch.empty((rows, hq, S), **f32)
+    if partial_o is None:
+        partial_o = torch.empty((rows, hq, S, dim), **f32)
+    _need(partial_m.shape == (rows, hq, S) and partial_d.shape == (rows, hq, S) and
+          partial_o.shape == (rows, hq, S, dim), "bad partial shapes")
+    _need(all(t.dtype == torch.float32 for t in (partial_m, partial_d, partial_o)),
+          "partials must be float32")
+    return partial_m, partial_d, partial_o
+
+
+def attn_sink_prefill_partials(q, k, v, sinks, cu_seqlens_q, cu_seqlens_kv,
+                               max_seqlen_q: int, group_size: int, num_splits: int,
+                               sm_scale: float | None = None, causal: bool = True,
+                               partial_m=None, partial_d=None, partial_o=None, stream=None):
+    """Split-KV ragged prefill: returns (partial_m, partial_d, partial_o) of
+    shapes [total_q, Hq, S], [total_q, Hq, S], [total_q, Hq, S, 64] for
+    attn_sink_merge (batch = total_q)."""
+    import torch
+    _dev(q, k, v, sinks, cu_seqlens_q, cu_seqlens_kv, partial_m, partial_d, partial_o)
+    dt = _dtype_code(q)
+    _need(k.dtype == q.dtype and v.dtype == q.dtype, "q, k, v dtypes differ")
+    _need(sinks.dtype == torch.float32, "sinks must be float32")
+    _need(cu_seqlens_q.dtype == torch.int32 and cu_seqlens_kv.dtype == torch.int32,
+          "cu_seqlens must be int32")
+    _need(q.dim() == 3 and k.dim() == 3 and v.shape == k.shape, "bad q/k/v shapes")
+    hkv = k.shape[1]
+    _need(q.shape[1] == hkv * group_size, "q heads != kv heads * group_size")
+    _need(sinks.numel() == q.shape[1], "sinks must have one value per query head")
+    batch = cu_seqlens_q.numel() - 1
+    _need(cu_seqlens_kv.numel() == batch + 1, "cu_seqlens length mismatch")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(q.shape[2])
+    S = int(num_splits)
+    pm, pd, po = _partials(q, S, partial_m, partial_d, partial_o)
+    rc = load_library().attn_sink_prefill_partials(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(sinks), _ptr(cu_seqlens_q), _ptr(cu_seqlens_kv),
+        batch, q.shape[0], k.shape[0], int(max_seqlen_q), hkv, int(group_size), q.shape[2],
+        float(sm_scale), int(bool(causal)), dt, S, _ptr(pm), _ptr(pd), _ptr(po),
+        _stream(stream))
+    _check(rc, "attn_sink_prefill_partials")
+    return pm, pd, po
+
+
+def attn_sink_prefill_paged(q, k_cache, v_cache, page_table, cu_seqlens_q, kv_lens, sinks,
+                            max_seqlen_q: int, group_size: int, sm_scale: float | None = None,
+                            causal: bool = True, num_splits: int = 1, partial_m=None,
+                            partial_d=None, partial_o=None, out=None, stream=None):
+    """Paged (chunked) prefill.  q [total_q, Hkv*G, 64] packed by cu_seqlens_q;
+    k_cache [pages, Hkv, 16, 64]; v_cache [pages, Hkv, 64, 16]; page_table
+    [B, max_pages] int32; kv_lens [B] int32 (keys in the cache, the new
+    tokens' included).  num_splits == 1 returns out; num_splits > 1 returns
+    (partial_m, partial_d, partial_o) for attn_sink_merge."""
+    import torch
+    _dev(q, k_cache, v_cache, page_table, cu_seqlens_q, kv_lens, sinks, partial_m, partial_d,
+         partial_o, out)
+    dt = _dtype_code(q)
+    _need(k_cache.dtype == q.dtype and v_cache.dtype == q.dtype, "dtype mismatch")
+    _need(page_table.dtype == torch.int32 and kv_lens.dtype == torch.int32 and
+          cu_seqlens_q.dtype == torch.int32, "page_table / cu_seqlens_q / kv_lens must be int32")
+    _need(k_cache.dim() == 4 and v_cache.dim() == 4, "caches must be 4-d")
+    num_pages, hkv, page, dim = k_cache.shape
+    _need(v_cache.shape == (num_pages, hkv, dim, page), "v_cache must be [pages, Hkv, D, P]")
+    _need(q.dim() == 3 and q.shape[1] == hkv * group_size, "q heads != kv heads * group_size")
+    batch = cu_seqlens_q.numel() - 1
+    _need(page_table.dim() == 2 and page_table.shape[0] == batch, "bad page_table")
+    _need(kv_lens.numel() == batch, "bad kv_lens")
+    _need(sinks.dtype == torch.float32 and sinks.numel() == q.shape[1], "bad sinks")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(dim)
+    S = int(num_splits)
+    if S == 1:
+        if out is None:
+            out = torch.empty_like(q)
+        _need(out.shape == q.shape and out.dtype == q.dtype, "bad out tensor")
+        pm = pd = po = None
+    else:
+        pm, pd, po = _partials(q, S, partial_m, partial_d, partial_o)
+    rc = load_library().attn_sink_prefill_paged(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table), _ptr(cu_seqlens_q),
+        _ptr(kv_lens), _ptr(sinks), batch, q.shape[0], int(max_seqlen_q), page_table.shape[1],
+        num_pages, hkv, int(group_size), dim, page, float(sm_scale), int(bool(causal)), dt, S,
+        _ptr(pm), _ptr(pd), _ptr(po), _ptr(out), _stream(stream))
+    _check(rc, "attn_sink_prefill_paged")
+    return out if S == 1 else (pm, pd, po)
 
 
 def attn_sink_decode_paged(q, k_cache, v_cache, page_table, kv_lens, sinks,

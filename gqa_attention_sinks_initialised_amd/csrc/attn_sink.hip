@@ -516,14 +516,56 @@ struct PrefillCfg {
   static constexpr int MIN_WAVES_PER_EU = DT == DT_F32 ? 1 : (RB == 2 ? 2 : 3);
 };
 
-template <int DT, int RB, int WAVES>
+// Arguments of the prefill kernels.  k / v are either the ragged key / value
+// arrays [total_kv, Hkv, D], located per sequence by cu_kv, or (PAGED) the
+// caches [pages, Hkv, P, D] / [pages, Hkv, D, P], located by page_table and
+// kv_lens.  Without SPLIT the kernel writes out; with SPLIT the key range of
+// each sequence is cut into `splits` chunks of whole 16-key units and the
+// kernel writes each chunk's partial state (m, d, o) to pm / pd / po.
+struct PrefillArgs {
+  const char* q;
+  const char* k;
+  const char* v;
+  const float* sinks;
+  const int32_t* cu_q;
+  const int32_t* cu_kv;
+  const int32_t* page_table;
+  const int32_t* kv_lens;
+  char* out;
+  float* pm;
+  float* pd;
+  float* po;
+  int total_q, total_kv, hkv, group, causal, n_qtiles, n_pairs, splits, max_pages, num_pages;
+  uint32_t cache_bytes;  // bytes of each paged cache
+  float qk_scale_log2;
+};
+
+// Keep the first n elements (16 / es of them) of a 16-byte vector, zero the
+// rest: the slots of a sequence's last page past its last key.
+__device__ __forceinline__ u32x4 keep_first(u32x4 x, int n, int es) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    unsigned int m;
+    if (es == 4)
+      m = e < n ? 0xffffffffu : 0u;
+    else
+      m = 2 * e + 1 < n ? 0xffffffffu : (2 * e < n ? 0x0000ffffu : 0u);
+    x[e] &= m;
+  }
+  return x;
+}
+
+template <int DT, int RB, int WAVES, bool PAGED, bool SPLIT>
 __global__ __launch_bounds__(64 * WAVES, (PrefillCfg<DT, RB, WAVES>::MIN_WAVES_PER_EU)) void
-prefill_kernel(const char* __restrict__ q, const char* __restrict__ k, const char* __restrict__ v,
-               const float* __restrict__ sinks, const int32_t* __restrict__ cu_q,
-               const int32_t* __restrict__ cu_kv, int total_q, int total_kv, int hkv, int group,
-               float qk_scale_log2, int causal, int n_qtiles, int n_pairs,
-               char* __restrict__ out) {
+prefill_kernel(const PrefillArgs a) {
   using Cfg = PrefillCfg<DT, RB, WAVES>;
+  const char* __restrict__ q = a.q;
+  const char* __restrict__ k = a.k;
+  const char* __restrict__ v = a.v;
+  const float* __restrict__ sinks = a.sinks;
+  const int total_q = a.total_q, hkv = a.hkv, group = a.group, causal = a.causal;
+  const int n_qtiles = a.n_qtiles, n_pairs = a.n_pairs;
+  const float qk_scale_log2 = a.qk_scale_log2;
   constexpr int ES = Cfg::ES, KROW = Cfg::KROW, VROW = Cfg::VROW, NT = Cfg::NT;
   constexpr int BK = 64;  // keys per tile
   __shared__ __attribute__((aligned(16))) char lds_k[2][BK * KROW * ES];
@@ -534,8 +576,12 @@ prefill_kernel(const char* __restrict__ q, const char* __restrict__ k, const cha
   // heaviest work first, and with a pair count that is a multiple of the 8
   // XCDs (workgroups go round-robin over XCDs) every tile of a pair lands on
   // the same XCD, whose L2 then holds that pair's K/V.
+  // With SPLIT, the chunks of one query tile are adjacent in dispatch order.
   const int pair = (int)(blockIdx.x % (unsigned)n_pairs);
-  const int tile = n_qtiles - 1 - (int)(blockIdx.x / (unsigned)n_pairs);
+  int slot = (int)(blockIdx.x / (unsigned)n_pairs);
+  const int split = SPLIT ? slot % a.splits : 0;
+  if constexpr (SPLIT) slot /= a.splits;
+  const int tile = n_qtiles - 1 - slot;
   const int kvh = pair % hkv, b = pair / hkv;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -544,19 +590,34 @@ prefill_kernel(const char* __restrict__ q, const char* __restrict__ k, const cha
   const int TW = Cfg::ROWS / group;  // tokens per wave
   const int TB = WAVES * TW;         // tokens per workgroup
 
-  const int q0 = clampi(cu_q[b], 0, total_q), q1 = clampi(cu_q[b + 1], q0, total_q);
-  const int k0 = clampi(cu_kv[b], 0, total_kv), k1 = clampi(cu_kv[b + 1], k0, total_kv);
-  const int Lq = q1 - q0, Lkv = k1 - k0;
+  const int q0 = clampi(a.cu_q[b], 0, total_q), q1 = clampi(a.cu_q[b + 1], q0, total_q);
+  int k0 = 0, Lkv;
+  if constexpr (PAGED) {
+    Lkv = clampi(a.kv_lens[b], 0, a.max_pages * kPage);
+  } else {
+    k0 = clampi(a.cu_kv[b], 0, a.total_kv);
+    Lkv = clampi(a.cu_kv[b + 1], k0, a.total_kv) - k0;
+  }
+  const int Lq = q1 - q0;
   const int t_begin = tile * TB;
   if (t_begin >= Lq) return;
   const int t_last = min(t_begin + TB, Lq) - 1;
   const int shift = Lkv - Lq;  // bottom-right causal alignment
 
+  // key chunk [c_lo, c_hi) of this workgroup: ceil(units / splits) whole
+  // 16-key units per chunk (page aligned when the keys are paged)
+  int c_lo = 0, c_hi = Lkv;
+  if constexpr (SPLIT) {
+    const int units = (Lkv + kPage - 1) / kPage, per = (units + a.splits - 1) / a.splits;
+    c_lo = min(split * per * kPage, Lkv);
+    c_hi = min(c_lo + per * kPage, Lkv);
+  }
+
   // keys this workgroup needs, and the key below which no valid row masks
   int n_keys = causal ? min(Lkv, t_last + shift + 1) : Lkv;
-  n_keys = max(n_keys, 0);
-  const int n_tiles = (n_keys + BK - 1) / BK;
-  const int lim_min = causal ? min(t_begin + shift, Lkv - 1) : Lkv - 1;
+  n_keys = min(max(n_keys, 0), c_hi);
+  const int n_tiles = n_keys > c_lo ? (n_keys - c_lo + BK - 1) / BK : 0;
+  const int lim_min = min(causal ? min(t_begin + shift, Lkv - 1) : Lkv - 1, c_hi - 1);
 
   // ---- rows of this lane, one per row block
   int lim[RB], head[RB], tok[RB];
@@ -568,7 +629,7 @@ prefill_kernel(const char* __restrict__ q, const char* __restrict__ k, const cha
     tok[rb] = t_begin + w * TW + tl;
     head[rb] = kvh * group + hl;
     valid[rb] = (tl < TW) && (tok[rb] < Lq);
-    lim[rb] = valid[rb] ? (causal ? min(tok[rb] + shift, Lkv - 1) : Lkv - 1) : -1;
+    lim[rb] = valid[rb] ? min(causal ? min(tok[rb] + shift, Lkv - 1) : Lkv - 1, c_hi - 1) : -1;
   }
 
   // ---- Q^T operand: lane group g owns dims [32g, 32g+32)
@@ -586,11 +647,12 @@ prefill_kernel(const char* __restrict__ q, const char* __restrict__ k, const cha
 
   // ---- running state per row (log2 units), starting from the sink: m = s,
   // d = e^(s - m) = 1 (0 for s = -inf), counted in lane group 0 only because
-  // d is summed over the two lanes of a row at the end
+  // d is summed over the two lanes of a row at the end.  Of a split key
+  // range only the first chunk carries the sink; the others start empty.
   float m_run[RB], d_run[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    const float s = valid[rb] ? sinks[head[rb]] : kNegInf;
+    const float s = (valid[rb] && split == 0) ? sinks[head[rb]] : kNegInf;
     m_run[rb] = s * kLog2e;
     d_run[rb] = (g == 0 && s != kNegInf) ? 1.f : 0.f;
   }
@@ -605,9 +667,11 @@ prefill_kernel(const char* __restrict__ q, const char* __restrict__ k, const cha
   // ---- K/V staging: global (buffer loads, zero past the sequence) -> regs -> LDS
   const uint32_t kv_row_bytes = (uint32_t)hkv * kHeadDim * ES;
   const __amdgpu_buffer_rsrc_t kr =
-      make_rsrc(k + (size_t)k0 * kv_row_bytes, (uint32_t)((size_t)Lkv * kv_row_bytes));
+      PAGED ? make_rsrc(k, a.cache_bytes)
+            : make_rsrc(k + (size_t)k0 * kv_row_bytes, (uint32_t)((size_t)Lkv * kv_row_bytes));
   const __amdgpu_buffer_rsrc_t vr =
-      make_rsrc(v + (size_t)k0 * kv_row_bytes, (uint32_t)((size_t)Lkv * kv_row_bytes));
+      PAGED ? make_rsrc(v, a.cache_bytes)
+            : make_rsrc(v + (size_t)k0 * kv_row_bytes, (uint32_t)((size_t)Lkv * kv_row_bytes));
   constexpr int CPR = kHeadDim * ES / 16;             // 16-byte chunks per key row
   constexpr int NCH = (BK * CPR + NT - 1) / NT;       // K chunks per thread
   constexpr int VITEMS = BK * CPR;                    // V chunks (one key row each)
@@ -616,8 +680,47 @@ prefill_kernel(const char* __restrict__ q, const char* __restrict__ k, const cha
   u32x4 stk[NCH], stv[NCV][VREG];
   const uint32_t head_off = (uint32_t)kvh * kHeadDim * ES;
 
+  // Paged: a tile of 64 keys is 4 whole pages (chunks start on a page).  K
+  // chunk c of a tile is 16 bytes of key row c / CPR; V chunk c is 16 bytes
+  // of dim row (c % (16 CPR)) / ES of the dim-major V page; both lie in page
+  // (c / (16 CPR)) of the tile.  Each thread's page ids are fetched one tile
+  // ahead so that the data loads never wait for the page table.
+  static_assert(NCV == NCH, "K and V chunks of a tile must pair up");
+  int pid[NCH];
+  auto fetch_ids = [&](int jt) {
+    if constexpr (PAGED) {
+#pragma unroll
+      for (int u = 0; u < NCH; ++u) {
+        const int lp = (c_lo + jt * BK) / kPage + (tid + NT * u) / (kPage * CPR);
+        const int id = (jt < n_tiles && lp * kPage < Lkv)
+                           ? a.page_table[(size_t)b * a.max_pages + lp] : -1;
+        pid[u] = (id >= 0 && id < a.num_pages) ? id : -1;  // bad ids: page skipped
+      }
+    }
+  };
+
   auto stage_load = [&](int jt) {
-    const int key0 = jt * BK;
+    const int key0 = c_lo + jt * BK;
+    if constexpr (PAGED) {
+#pragma unroll
+      for (int u = 0; u < NCH; ++u) {
+        const int c = tid + NT * u;
+        const int key = c / CPR, part = c % CPR;
+        const int vrem = c % (kPage * CPR), dim = vrem / ES, vp = vrem % ES;
+        const int tp = c / (kPage * CPR);
+        if (c < BK * CPR && pid[u] >= 0) {
+          const uint32_t pg = (uint32_t)pid[u] * hkv + kvh;
+          stk[u] = buf_load16(kr, (pg * kPage + (key & (kPage - 1))) * (kHeadDim * ES) + part * 16);
+          const u32x4 x = buf_load16(vr, (pg * kHeadDim + dim) * (kPage * ES) + vp * 16);
+          stv[u][0] = keep_first(x, Lkv - (key0 + tp * kPage + vp * (16 / ES)), ES);
+        } else {
+          stk[u] = u32x4{0, 0, 0, 0};
+          stv[u][0] = u32x4{0, 0, 0, 0};
+        }
+      }
+      fetch_ids(jt + 1);
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < NCH; ++u) {
       const int c = tid + NT * u, key = c / CPR, part = c % CPR;
@@ -649,6 +752,28 @@ prefill_kernel(const char* __restrict__ q, const char* __restrict__ k, const cha
         else
           *reinterpret_cast<u32x4*>(kd + (key * KROW + part * (16 / ES)) * ES) = stk[u];
       }
+    }
+    if constexpr (PAGED) {
+      // V^T tile [64 dims][64 keys].  bf16: 128-byte rows of 4-key (8-byte)
+      // granules, granule g of dim row d at slot g ^ ((d >> 1) & 15), so the
+      // 32 dim rows one ds_read_b64 touches fall on distinct banks.  fp32:
+      // rows padded by 16 bytes.
+#pragma unroll
+      for (int u = 0; u < NCV; ++u) {
+        const int c = tid + NT * u;
+        if (c >= VITEMS) continue;
+        const int vrem = c % (kPage * CPR), dim = vrem / ES, vp = vrem % ES;
+        const int tp = c / (kPage * CPR);
+        const u32x4 x = stv[u][0];
+        if constexpr (DT == DT_BF16) {
+          const int gr = 4 * tp + 2 * vp, sw = (dim >> 1) & 15;
+          *reinterpret_cast<u32x2*>(vd + dim * 128 + 8 * (gr ^ sw)) = u32x2{x[0], x[1]};
+          *reinterpret_cast<u32x2*>(vd + dim * 128 + 8 * ((gr + 1) ^ sw)) = u32x2{x[2], x[3]};
+        } else {
+          *reinterpret_cast<u32x4*>(vd + (dim * VROW + tp * kPage + 4 * vp) * ES) = x;
+        }
+      }
+      return;
     }
 #pragma unroll
     for (int u = 0; u < NCV; ++u) {
@@ -720,11 +845,11 @@ prefill_kernel(const char* __restrict__ q, const char* __restrict__ k, const cha
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       if constexpr (decltype(masked)::value) {
-        // key = jt*BK + kb*32 + 4g + off(r) with off(r) = 8*(r/4) + r%4 a
+        // key = c_lo + jt*BK + kb*32 + 4g + off(r), off(r) = 8*(r/4) + r%4 a
         // constant: compare off(r) with one per-lane threshold per key block
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          const int thr = lim[rb] - (jt * BK + kb * 32 + 4 * g);
+          const int thr = lim[rb] - (c_lo + jt * BK + kb * 32 + 4 * g);
 #pragma unroll
           for (int r = 0; r < 16; ++r)
             sacc[kb][rb][r] = (8 * (r >> 2) + (r & 3) > thr) ? kNegInf : sacc[kb][rb][r];
@@ -785,6 +910,8 @@ prefill_kernel(const char* __restrict__ q, const char* __restrict__ k, const cha
       // source lane s of each 16-lane group points at V[kbase + s/4][dim0 +
       // 4*(s%4)]; after the transposing read lane i holds V[kbase + 0..3]
       // [dim0 + i] with dim0 + i = 32*db + lane%32
+      // (paged: the V^T tile is dim-major already; lane (g, col) reads the
+      // 4-key granules 8kb + 4hh + g and that + 2 of dim row 32db + col)
       typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
       const int sl = lane & 15;
 #pragma unroll
@@ -795,6 +922,13 @@ prefill_kernel(const char* __restrict__ q, const char* __restrict__ k, const cha
           u32x4 vf[2];
 #pragma unroll
           for (int db = 0; db < 2; ++db) {
+            if constexpr (PAGED) {
+              const int dim = 32 * db + col, sw = (dim >> 1) & 15, g1 = 8 * kb + 4 * hh + g;
+              const u32x2 lo = *reinterpret_cast<const u32x2*>(vd + dim * 128 + 8 * (g1 ^ sw));
+              const u32x2 hi = *reinterpret_cast<const u32x2*>(vd + dim * 128 + 8 * ((g1 + 2) ^ sw));
+              vf[db] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+              continue;
+            }
             const int dim = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (sl & 3);
             const int chunk = dim >> 3, sub = 2 * (dim & 7);
             const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -836,8 +970,9 @@ prefill_kernel(const char* __restrict__ q, const char* __restrict__ k, const cha
   // Tiles below n_plain need no mask for any valid row of the workgroup; the
   // remaining (diagonal / ragged-tail) tiles run the masked body.  Two loops
   // keep the mask arithmetic out of the common path.
-  const int n_plain = min(n_tiles, max(0, (lim_min + 1) / BK));
+  const int n_plain = min(n_tiles, max(0, (lim_min + 1 - c_lo) / BK));
   if (n_tiles > 0) {
+    fetch_ids(0);
     stage_load(0);
     stage_store(0);
     __syncthreads();
@@ -858,13 +993,30 @@ prefill_kernel(const char* __restrict__ q, const char* __restrict__ k, const cha
     }
   }
 
-  // ---- epilogue: out = O / d, rows of this lane, dims 32db + 8qd + 4g + 0..3
+  // ---- epilogue: out = O / d (SPLIT: the state m, d, O of this chunk, m in
+  // natural-log units), rows of this lane, dims 32db + 8qd + 4g + 0..3
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const float dsum = xor_sum(d_run[rb], 32);
     if (!valid[rb]) continue;
+    if constexpr (SPLIT) {
+      const size_t st = (((size_t)q0 + tok[rb]) * hq + head[rb]) * a.splits + split;
+      if (g == 0) {
+        a.pm[st] = m_run[rb] * kLn2;
+        a.pd[st] = dsum;
+      }
+      float* po = a.po + st * kHeadDim;
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd)
+          *reinterpret_cast<f32x4*>(po + 32 * db + 8 * qd + 4 * g) =
+              f32x4{acc_o[db][rb][4 * qd + 0], acc_o[db][rb][4 * qd + 1],
+                    acc_o[db][rb][4 * qd + 2], acc_o[db][rb][4 * qd + 3]};
+      continue;
+    }
     const float inv = dsum > 0.f ? 1.f / dsum : 0.f;
-    char* orow = out + (((size_t)q0 + tok[rb]) * hq + head[rb]) * kHeadDim * ES;
+    char* orow = a.out + (((size_t)q0 + tok[rb]) * hq + head[rb]) * kHeadDim * ES;
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
@@ -908,6 +1060,100 @@ constexpr int kPrefillWaves = ATTN_SINK_PREFILL_WAVES;
 constexpr int kDecodeWaves = ATTN_SINK_DECODE_WAVES;
 constexpr int kDecodeUnroll = ATTN_SINK_DECODE_UNROLL;
 
+// Launch the prefill kernel for (dtype, key source, output form): a 1-D grid
+// of query tiles x (sequence, kv head) pairs x key chunks.
+template <bool PAGED, bool SPLIT>
+int launch_prefill(PrefillArgs a, int dtype, int batch, int max_seqlen_q, hipStream_t s) {
+  if ((int64_t)batch * a.hkv > INT32_MAX) return ATTN_SINK_ERR_UNSUPPORTED;
+  a.n_pairs = batch * a.hkv;
+  const int waves = dtype == ATTN_SINK_BF16 ? kPrefillWaves : 4;
+  const int tb = waves * (64 / a.group);  // waves of 64 rows
+  a.n_qtiles = (max_seqlen_q + tb - 1) / tb;
+  const int64_t blocks = (int64_t)a.n_qtiles * a.n_pairs * (SPLIT ? a.splits : 1);
+  if (blocks > INT32_MAX) return ATTN_SINK_ERR_UNSUPPORTED;
+  const dim3 grid((unsigned)blocks);
+  if (dtype == ATTN_SINK_F32)
+    hipLaunchKernelGGL((prefill_kernel<DT_F32, 2, 4, PAGED, SPLIT>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((prefill_kernel<DT_BF16, 2, kPrefillWaves, PAGED, SPLIT>), grid,
+                       dim3(64 * kPrefillWaves), 0, s, a);
+  return launch_status();
+}
+
+// Checks shared by the prefill entry points (query side and scalars).
+int check_prefill_common(const void* q, const float* sinks, const int32_t* cu_seqlens_q,
+                         int batch, int total_q, int max_seqlen_q, int num_kv_heads,
+                         int group_size, int head_dim, float sm_scale, int causal, int dtype) {
+  if (!sinks || !cu_seqlens_q || (!q && total_q != 0)) return ATTN_SINK_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(sinks, 4) || !aligned(cu_seqlens_q, 4))
+    return ATTN_SINK_ERR_INVALID_ARG;
+  if (batch < 0 || total_q < 0 || max_seqlen_q < 0 || num_kv_heads < 1 || group_size < 1 ||
+      head_dim < 1 || (causal != 0 && causal != 1) ||
+      (dtype != ATTN_SINK_F32 && dtype != ATTN_SINK_BF16) || !finite_positive(sm_scale))
+    return ATTN_SINK_ERR_INVALID_ARG;
+  if (head_dim != kHeadDim || group_size > 64) return ATTN_SINK_ERR_UNSUPPORTED;
+  const int es = dtype == ATTN_SINK_BF16 ? 2 : 4;
+  // buffer offsets are 32-bit: each whole tensor must stay below 4 GiB
+  if ((int64_t)total_q * num_kv_heads * group_size * kHeadDim * es >= (int64_t)1 << 32)
+    return ATTN_SINK_ERR_UNSUPPORTED;
+  return ATTN_SINK_OK;
+}
+
+// Checks of the split-KV partial outputs of a prefill entry point.
+int check_partials(int num_splits, const float* pm, const float* pd, const float* po) {
+  if (num_splits < 1 || num_splits > 65536) return ATTN_SINK_ERR_INVALID_ARG;
+  if (!pm || !pd || !po) return ATTN_SINK_ERR_INVALID_ARG;
+  if (!aligned(pm, 4) || !aligned(pd, 4) || !aligned(po, 16)) return ATTN_SINK_ERR_INVALID_ARG;
+  return ATTN_SINK_OK;
+}
+
+// Ragged prefill: with pm == NULL the output goes to out (one chunk), else
+// the partial states of num_splits chunks go to pm / pd / po.
+int attn_sink_prefill_partials_impl(const void* q, const void* k, const void* v,
+                                    const float* sinks, const int32_t* cu_seqlens_q,
+                                    const int32_t* cu_seqlens_kv, int batch, int total_q,
+                                    int total_kv, int max_seqlen_q, int num_kv_heads,
+                                    int group_size, int head_dim, float sm_scale, int causal,
+                                    int dtype, int num_splits, float* pm, float* pd, float* po,
+                                    void* out, void* stream) {
+  const int rc = check_prefill_common(q, sinks, cu_seqlens_q, batch, total_q, max_seqlen_q,
+                                      num_kv_heads, group_size, head_dim, sm_scale, causal,
+                                      dtype);
+  if (rc != ATTN_SINK_OK) return rc;
+  // k/v may be NULL only for an empty key set, out only for an empty query set
+  if (!cu_seqlens_kv || ((!k || !v) && total_kv != 0) || total_kv < 0 ||
+      (!pm && !out && total_q != 0))
+    return ATTN_SINK_ERR_INVALID_ARG;
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(cu_seqlens_kv, 4))
+    return ATTN_SINK_ERR_INVALID_ARG;
+  const int es = dtype == ATTN_SINK_BF16 ? 2 : 4;
+  if ((int64_t)total_kv * num_kv_heads * kHeadDim * es >= (int64_t)1 << 32 ||
+      (int64_t)total_kv + (int64_t)kPage * num_splits > INT32_MAX)
+    return ATTN_SINK_ERR_UNSUPPORTED;
+  if (batch == 0 || total_q == 0 || max_seqlen_q == 0) return ATTN_SINK_OK;
+  PrefillArgs a{};
+  a.q = (const char*)q;
+  a.k = (const char*)k;
+  a.v = (const char*)v;
+  a.sinks = sinks;
+  a.cu_q = cu_seqlens_q;
+  a.cu_kv = cu_seqlens_kv;
+  a.out = (char*)out;
+  a.pm = pm;
+  a.pd = pd;
+  a.po = po;
+  a.total_q = total_q;
+  a.total_kv = total_kv;
+  a.hkv = num_kv_heads;
+  a.group = group_size;
+  a.causal = causal;
+  a.splits = num_splits;
+  a.qk_scale_log2 = sm_scale * kLog2e;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return pm ? launch_prefill<false, true>(a, dtype, batch, max_seqlen_q, s)
+            : launch_prefill<false, false>(a, dtype, batch, max_seqlen_q, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -927,46 +1173,82 @@ int attn_sink_prefill(const void* q, const void* k, const void* v, const float* 
                       int total_q, int total_kv, int max_seqlen_q, int num_kv_heads,
                       int group_size, int head_dim, float sm_scale, int causal, int dtype,
                       void* out, void* stream) {
-  // q/out may be NULL only for an empty query set, k/v only for an empty key set
-  if (!sinks || !cu_seqlens_q || !cu_seqlens_kv || ((!q || !out) && total_q != 0) ||
-      ((!k || !v) && total_kv != 0))
+  return attn_sink_prefill_partials_impl(q, k, v, sinks, cu_seqlens_q, cu_seqlens_kv, batch,
+                                         total_q, total_kv, max_seqlen_q, num_kv_heads,
+                                         group_size, head_dim, sm_scale, causal, dtype, 1,
+                                         nullptr, nullptr, nullptr, out, stream);
+}
+
+int attn_sink_prefill_partials(const void* q, const void* k, const void* v, const float* sinks,
+                               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+                               int batch, int total_q, int total_kv, int max_seqlen_q,
+                               int num_kv_heads, int group_size, int head_dim, float sm_scale,
+                               int causal, int dtype, int num_splits, float* partial_m,
+                               float* partial_d, float* partial_o, void* stream) {
+  const int rc = check_partials(num_splits, partial_m, partial_d, partial_o);
+  if (rc != ATTN_SINK_OK) return rc;
+  return attn_sink_prefill_partials_impl(q, k, v, sinks, cu_seqlens_q, cu_seqlens_kv, batch,
+                                         total_q, total_kv, max_seqlen_q, num_kv_heads,
+                                         group_size, head_dim, sm_scale, causal, dtype,
+                                         num_splits, partial_m, partial_d, partial_o, nullptr,
+                                         stream);
+}
+
+int attn_sink_prefill_paged(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* page_table, const int32_t* cu_seqlens_q,
+                            const int32_t* kv_lens, const float* sinks, int batch, int total_q,
+                            int max_seqlen_q, int max_pages_per_seq, int num_pages,
+                            int num_kv_heads, int group_size, int head_dim, int page_size,
+                            float sm_scale, int causal, int dtype, int num_splits,
+                            float* partial_m, float* partial_d, float* partial_o, void* out,
+                            void* stream) {
+  int rc = check_prefill_common(q, sinks, cu_seqlens_q, batch, total_q, max_seqlen_q,
+                                num_kv_heads, group_size, head_dim, sm_scale, causal, dtype);
+  if (rc != ATTN_SINK_OK) return rc;
+  // the caches may be NULL only when they hold no page
+  if (!page_table || !kv_lens || ((!k_cache || !v_cache) && num_pages != 0))
     return ATTN_SINK_ERR_INVALID_ARG;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
-      !aligned(sinks, 4) || !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_kv, 4))
+  if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(page_table, 4) ||
+      !aligned(kv_lens, 4))
     return ATTN_SINK_ERR_INVALID_ARG;
-  if (batch < 0 || total_q < 0 || total_kv < 0 || max_seqlen_q < 0 || num_kv_heads < 1 ||
-      group_size < 1 || head_dim < 1 || (causal != 0 && causal != 1) ||
-      (dtype != ATTN_SINK_F32 && dtype != ATTN_SINK_BF16) || !finite_positive(sm_scale))
-    return ATTN_SINK_ERR_INVALID_ARG;
-  if (head_dim != kHeadDim || group_size > 64) return ATTN_SINK_ERR_UNSUPPORTED;
-  if ((int64_t)batch * num_kv_heads > INT32_MAX) return ATTN_SINK_ERR_UNSUPPORTED;
+  if (num_splits == 1) {
+    if ((!out && total_q != 0) || !aligned(out, 16)) return ATTN_SINK_ERR_INVALID_ARG;
+  } else {
+    rc = check_partials(num_splits, partial_m, partial_d, partial_o);
+    if (rc != ATTN_SINK_OK) return rc;
+  }
+  if (max_pages_per_seq < 1 || num_pages < 0 || page_size < 1) return ATTN_SINK_ERR_INVALID_ARG;
+  if (page_size != kPage) return ATTN_SINK_ERR_UNSUPPORTED;
   const int es = dtype == ATTN_SINK_BF16 ? 2 : 4;
-  const int64_t hq = (int64_t)num_kv_heads * group_size;
-  // buffer offsets are 32-bit: each whole tensor must stay below 4 GiB
-  if ((int64_t)total_q * hq * kHeadDim * es >= (int64_t)1 << 32 ||
-      (int64_t)total_kv * num_kv_heads * kHeadDim * es >= (int64_t)1 << 32)
+  const int64_t cache_bytes = (int64_t)num_pages * num_kv_heads * kPage * kHeadDim * es;
+  if (cache_bytes >= (int64_t)1 << 32 ||
+      (int64_t)max_pages_per_seq * kPage + (int64_t)kPage * num_splits > INT32_MAX)
     return ATTN_SINK_ERR_UNSUPPORTED;
   if (batch == 0 || total_q == 0 || max_seqlen_q == 0) return ATTN_SINK_OK;
-  const float qk = sm_scale * kLog2e;
+  PrefillArgs a{};
+  a.q = (const char*)q;
+  a.k = (const char*)k_cache;
+  a.v = (const char*)v_cache;
+  a.sinks = sinks;
+  a.cu_q = cu_seqlens_q;
+  a.page_table = page_table;
+  a.kv_lens = kv_lens;
+  a.out = (char*)out;
+  a.pm = partial_m;
+  a.pd = partial_d;
+  a.po = partial_o;
+  a.total_q = total_q;
+  a.hkv = num_kv_heads;
+  a.group = group_size;
+  a.causal = causal;
+  a.splits = num_splits;
+  a.max_pages = max_pages_per_seq;
+  a.num_pages = num_pages;
+  a.cache_bytes = (uint32_t)cache_bytes;
+  a.qk_scale_log2 = sm_scale * kLog2e;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const int n_pairs = batch * num_kv_heads;
-  const int waves = dtype == ATTN_SINK_BF16 ? kPrefillWaves : 4;
-  const int tb = waves * (64 / group_size);  // waves of 64 rows
-  const int n_qtiles = (max_seqlen_q + tb - 1) / tb;
-  if ((int64_t)n_qtiles * n_pairs > INT32_MAX) return ATTN_SINK_ERR_UNSUPPORTED;
-  const dim3 grid(n_qtiles * n_pairs);
-  if (dtype == ATTN_SINK_F32)
-    hipLaunchKernelGGL((prefill_kernel<DT_F32, 2, 4>), grid, dim3(256), 0, s, (const char*)q,
-                       (const char*)k, (const char*)v, sinks, cu_seqlens_q, cu_seqlens_kv,
-                       total_q, total_kv, num_kv_heads, group_size, qk, causal, n_qtiles,
-                       n_pairs, (char*)out);
-  else
-    hipLaunchKernelGGL((prefill_kernel<DT_BF16, 2, kPrefillWaves>), grid, dim3(64 * kPrefillWaves),
-                       0, s, (const char*)q,
-                       (const char*)k, (const char*)v, sinks, cu_seqlens_q, cu_seqlens_kv,
-                       total_q, total_kv, num_kv_heads, group_size, qk, causal, n_qtiles,
-                       n_pairs, (char*)out);
-  return launch_status();
+  return num_splits == 1 ? launch_prefill<true, false>(a, dtype, batch, max_seqlen_q, s)
+                         : launch_prefill<true, true>(a, dtype, batch, max_seqlen_q, s);
 }
 
 int attn_sink_decode_paged(const void* q, const void* k_cache, const void* v_cache,

@@ -86,6 +86,74 @@ int attn_sink_prefill(const void *q, const void *k, const void *v,
                       int dtype, void *out, void *stream);
 
 /*
+ * Split-KV ragged prefill: the partial states of each query row over S
+ * chunks of its sequence's key range, for attn_sink_merge to combine.  For
+ * few query tiles against long key ranges this fills the GPU.
+ * Passage: "GPT-OSS on Day 0", section "Kernels for GPT-OSS / Sink
+ * Attention" (blocks along the key length, the sink in the first only).
+ *
+ *   q, k, v, sinks, cu_seqlens_*, sizes, sm_scale, causal: as in
+ *         attn_sink_prefill
+ *   num_splits S in 1..65536: sequence b's Lkv keys are cut into chunks of
+ *         ceil(ceil(Lkv/16)/S) whole 16-key units; chunk c of a query row
+ *         holds the keys of chunk c that the row can see.  Chunk 0 carries
+ *         the sink: an empty chunk 0 yields (s_h, 1, 0), an empty chunk
+ *         c > 0 yields (-inf, 0, 0).
+ *   partial_m, partial_d [total_q, Hkv*G, S] fp32 (m in natural-log units)
+ *   partial_o            [total_q, Hkv*G, S, D] fp32, unnormalised
+ *         (relative to m); (m, d, o) is one of many equivalent states, since
+ *         any m with d and o taken relative to it merges to the same result:
+ *         m + ln d and o / d are unique.
+ * attn_sink_merge(partial_m, partial_d, partial_o, total_q, Hkv*G, S, ...)
+ * then yields what attn_sink_prefill writes.
+ */
+int attn_sink_prefill_partials(const void *q, const void *k, const void *v,
+                               const float *sinks, const int32_t *cu_seqlens_q,
+                               const int32_t *cu_seqlens_kv, int batch,
+                               int total_q, int total_kv, int max_seqlen_q,
+                               int num_kv_heads, int group_size, int head_dim,
+                               float sm_scale, int causal, int dtype,
+                               int num_splits, float *partial_m,
+                               float *partial_d, float *partial_o,
+                               void *stream);
+
+/*
+ * Paged (chunked) prefill: several new query tokens per sequence against
+ * the paged key/value cache that already holds them, optionally split along
+ * the key length.
+ * Passage: "Fast embeddings on GPUs", section "ROSE" (prefill over a paged
+ * cache); "GPT-OSS on Day 0", section "Kernels for GPT-OSS / Sink
+ * Attention" (one kernel design for prefill and decode; the split rule).
+ *
+ *   q          [total_q, Hkv*G, D] dtype, sequences packed (cu_seqlens_q)
+ *   k_cache, v_cache, page_table, num_pages, page_size: as in
+ *              attn_sink_decode_paged
+ *   kv_lens    [batch] int32: keys in the cache, the new tokens' included,
+ *              clamped to [0, max_pages_per_seq*page_size].  The Lq queries
+ *              of a sequence are its last Lq positions: with causal = 1 row
+ *              i sees keys j <= i + kv_len - Lq (bottom-right alignment).
+ *   sinks, group_size (1..64), head_dim, sm_scale, max_seqlen_q: as in
+ *              attn_sink_prefill
+ *   num_splits S == 1: writes out [total_q, Hkv*G, D] dtype; partials may
+ *              be NULL.  S > 1 (up to 65536): chunks of whole pages as in
+ *              attn_sink_decode_paged, clipped to each row's visible keys;
+ *              writes partial_m, partial_d [total_q, Hkv*G, S] and
+ *              partial_o [total_q, Hkv*G, S, D] as attn_sink_prefill_partials
+ *              does; out is not touched and may be NULL.
+ * q and out may be NULL when total_q == 0; the caches when num_pages == 0.
+ */
+int attn_sink_prefill_paged(const void *q, const void *k_cache,
+                            const void *v_cache, const int32_t *page_table,
+                            const int32_t *cu_seqlens_q, const int32_t *kv_lens,
+                            const float *sinks, int batch, int total_q,
+                            int max_seqlen_q, int max_pages_per_seq,
+                            int num_pages, int num_kv_heads, int group_size,
+                            int head_dim, int page_size, float sm_scale,
+                            int causal, int dtype, int num_splits,
+                            float *partial_m, float *partial_d,
+                            float *partial_o, void *out, void *stream);
+
+/*
  * Paged decode (one query token per sequence) with sinks, optionally split
  * along the key length.
  * Passage: "GPT-OSS on Day 0", section "Kernels for GPT-OSS / Sink

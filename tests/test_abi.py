@@ -31,10 +31,10 @@ def L():
     return m.load_library()
 
 
-def test_header_declares_the_three_entry_points():
+def test_header_declares_the_entry_points():
     names = _declared_functions()
-    for n in ("attn_sink_prefill", "attn_sink_decode_paged", "attn_sink_merge",
-              "attn_sink_status_string"):
+    for n in ("attn_sink_prefill", "attn_sink_prefill_partials", "attn_sink_prefill_paged",
+              "attn_sink_decode_paged", "attn_sink_merge", "attn_sink_status_string"):
         assert n in names
 
 
@@ -73,6 +73,22 @@ def _decode(L, **kw):
     return L.attn_sink_decode_paged(*args.values())
 
 
+def _prefill_partials(L, **kw):
+    args = dict(q=A, k=A, v=A, sinks=A, cq=A, ck=A, batch=1, tq=4, tkv=4, maxq=4, hkv=1,
+                group=1, dim=64, scale=0.125, causal=1, dtype=1, splits=3, pm=A, pd=A, po=A,
+                stream=None)
+    args.update(kw)
+    return L.attn_sink_prefill_partials(*args.values())
+
+
+def _prefill_paged(L, **kw):
+    args = dict(q=A, kc=A, vc=A, pt=A, cq=A, lens=A, sinks=A, batch=1, tq=4, maxq=4, maxp=4,
+                npages=4, hkv=1, group=1, dim=64, page=16, scale=0.125, causal=1, dtype=1,
+                splits=1, pm=None, pd=None, po=None, out=A, stream=None)
+    args.update(kw)
+    return L.attn_sink_prefill_paged(*args.values())
+
+
 def _merge(L, **kw):
     args = dict(pm=A, pd=A, po=A, batch=1, hq=1, splits=2, dim=64, dtype=1, out=A, stream=None)
     args.update(kw)
@@ -108,6 +124,33 @@ def test_prefill_validation(L, kw, code):
     (dict(batch=0), OK), (dict(batch=0, splits=3, pm=A, pd=A, po=A, out=None), OK)])
 def test_decode_validation(L, kw, code):
     assert _decode(L, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(pm=None), INVALID), (dict(pd=None), INVALID), (dict(po=MIS), INVALID),
+    (dict(splits=0), INVALID), (dict(splits=65537), INVALID), (dict(q=None), INVALID),
+    (dict(k=None), INVALID), (dict(ck=None), INVALID), (dict(causal=3), INVALID),
+    (dict(scale=float("inf")), INVALID), (dict(dim=96), UNSUPPORTED),
+    (dict(group=65), UNSUPPORTED), (dict(k=None, v=None, tkv=0, batch=0), OK),
+    (dict(batch=0), OK), (dict(tq=0, q=None), OK), (dict(maxq=0), OK)])
+def test_prefill_partials_validation(L, kw, code):
+    assert _prefill_partials(L, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INVALID), (dict(pt=None), INVALID), (dict(lens=None), INVALID),
+    (dict(cq=None), INVALID), (dict(kc=None), INVALID), (dict(out=None), INVALID),
+    (dict(splits=0), INVALID), (dict(splits=4), INVALID),          # splits > 1 needs partials
+    (dict(splits=4, pm=A, pd=A, po=MIS, out=None), INVALID), (dict(kc=MIS), INVALID),
+    (dict(maxp=0), INVALID), (dict(npages=-1), INVALID), (dict(causal=-1), INVALID),
+    (dict(dtype=2), INVALID), (dict(scale=0.0), INVALID),
+    (dict(dim=32), UNSUPPORTED), (dict(page=8), UNSUPPORTED), (dict(group=80), UNSUPPORTED),
+    (dict(maxp=1 << 27), UNSUPPORTED), (dict(npages=1 << 20, hkv=8), UNSUPPORTED),
+    (dict(kc=None, vc=None, npages=0, batch=0), OK), (dict(batch=0), OK),
+    (dict(tq=0, q=None, out=None), OK),
+    (dict(batch=0, splits=3, pm=A, pd=A, po=A, out=None), OK)])
+def test_prefill_paged_validation(L, kw, code):
+    assert _prefill_paged(L, **kw) == code
 
 
 @pytest.mark.parametrize("kw,code", [

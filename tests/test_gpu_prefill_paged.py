@@ -1,0 +1,233 @@
+"""GPU parity of paged (chunked) prefill and split-KV prefill (MI355X).
+
+Paged prefill runs several new query tokens per sequence against the paged
+cache (page "Fast embeddings on GPUs", section "ROSE"); split-KV prefill cuts
+each sequence's key range into chunks whose partial states attn_sink_merge
+combines, the sink carried by chunk 0 only (page "GPT-OSS on Day 0", section
+"Kernels for GPT-OSS / Sink Attention").
+
+A chunk's state (m, d, o) is one of many equivalent ones (the kernel keeps a
+reference max that may trail the true max by a bounded amount), so partial
+states are compared through what is unique: m + ln d and o / d, with the
+empty states (-inf, 0, 0) and chunk 0's sink-only state (s, 1, 0) exact.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from helpers import assert_close, sample_prefill_rows, tol_for
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+NAN = float("nan")
+
+
+def _dev(d):
+    return {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+
+
+def paged_case(lens_q, lens_kv, hq, hkv, dtype, seed, fill=NAN, **kw):
+    """Ragged inputs plus the same keys scattered into a paged cache whose
+    unused slots and pages hold `fill`."""
+    kw.setdefault("sink_std", 1.5)
+    d = workloads.prefill_inputs(lens_q, lens_kv, hq=hq, hkv=hkv, dtype=dtype, seed=seed, **kw)
+    d.update(workloads.pack_paged(d["k"], d["v"], d["lens_kv"], seed=seed + 1,
+                                  extra_pages=3, fill=fill))
+    return d
+
+
+def run_paged(lib, d, causal=True, splits=1):
+    dd = _dev(d)
+    r = lib.attn_sink_prefill_paged(dd["q"], dd["k_cache"], dd["v_cache"], dd["page_table"],
+                                    dd["cu_seqlens_q"], dd["kv_lens"], dd["sinks"],
+                                    max(d["lens_q"] + [0]), d["group"], d["sm_scale"], causal,
+                                    num_splits=splits)
+    torch.cuda.synchronize()
+    return r.cpu() if splits == 1 else tuple(t.cpu() for t in r)
+
+
+def run_ragged_partials(lib, d, causal, splits):
+    dd = _dev(d)
+    r = lib.attn_sink_prefill_partials(dd["q"], dd["k"], dd["v"], dd["sinks"],
+                                       dd["cu_seqlens_q"], dd["cu_seqlens_kv"],
+                                       max(d["lens_q"] + [0]), d["group"], splits,
+                                       d["sm_scale"], causal)
+    torch.cuda.synchronize()
+    return tuple(t.cpu() for t in r)
+
+
+def oracle_paged(d, causal=True, splits=0, rows=None):
+    return oracle.prefill_paged(d["q"], d["k_cache"], d["v_cache"], d["page_table"],
+                                d["cu_seqlens_q"], d["kv_lens"], d["sinks"], d["group"],
+                                d["sm_scale"], causal, splits=splits, rows=rows)
+
+
+def check_partials(got, ref, dtype, sinks, what):
+    """Compare kernel partial states with the oracle's through their unique
+    parts; empty and sink-only states must be exact.  sinks broadcasts
+    against the state shape without its split axis."""
+    gm, gd, go = (t.double().numpy() for t in got)
+    rm, rd, ro = ref
+    empty = rm == -math.inf
+    np.testing.assert_array_equal(gm == -math.inf, empty, err_msg=what + ": empty pattern")
+    np.testing.assert_array_equal(gd[empty], 0.0)
+    np.testing.assert_array_equal(go[empty], 0.0)
+    # chunk 0 with no visible key and a finite sink: exactly (s, 1, 0)
+    sink_only = (rd == 1.0) & np.all(ro == 0.0, axis=-1) & ~empty
+    sink_only[..., 1:] = False
+    if sink_only.any():
+        s = np.broadcast_to(sinks.double().numpy()[..., None], rm.shape)
+        np.testing.assert_array_equal(gd[sink_only], 1.0)
+        np.testing.assert_array_equal(go[sink_only], 0.0)
+        np.testing.assert_allclose(gm[sink_only], s[sink_only], rtol=1e-6, atol=1e-6)
+    live = ~empty
+    lse_tol = 1e-2 if dtype == torch.bfloat16 else 2e-5
+    np.testing.assert_allclose(gm[live] + np.log(gd[live]), rm[live] + np.log(rd[live]),
+                               rtol=0, atol=lse_tol, err_msg=what + ": m + ln d")
+    atol, rtol = tol_for(dtype)
+    on = go[live] / gd[live][:, None]
+    rn = ro[live] / rd[live][:, None]
+    bad = np.abs(on - rn) > atol + rtol * np.abs(rn)
+    assert not bad.any(), "%s: o/d out of tolerance at %d elements" % (what, int(bad.sum()))
+
+
+CASES = [
+    # lens_q, lens_kv, hq, hkv, causal
+    ([1], [1], 8, 2, True),
+    ([5, 20, 1], [37, 20, 64], 8, 2, True),          # new tokens at the end of a cache
+    ([64, 65], [200, 65], 8, 1, True),               # page-unaligned starts of the queries
+    ([130, 7], [1000, 300], 16, 2, True),            # short chunk against a long cache
+    ([50, 1], [20, 80], 4, 2, True),                 # Lq > Lkv: leading rows see no key
+    ([70, 129], [150, 3], 8, 4, False),              # non-causal
+    ([0, 40, 0, 9], [0, 40, 5, 9], 4, 1, True),      # empty sequences / empty cache
+    ([300], [300], 64, 1, True),                     # group 64
+    ([97], [130], 6, 2, True),                       # group 3
+    ([129], [257], 2, 2, True),                      # group 1
+]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_paged_prefill_sweep_matches_oracle(lib, dtype, case):
+    lens_q, lens_kv, hq, hkv, causal = CASES[case]
+    d = paged_case(lens_q, lens_kv, hq, hkv, dtype, seed=40 + case)
+    out = run_paged(lib, d, causal)
+    assert_close(out, oracle_paged(d, causal), dtype, "paged case %d" % case)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_paged_equals_ragged_kernel_bitwise(lib, dtype):
+    """The paged kernel reads the same K/V values into the same MFMA
+    operands as the ragged kernel, so the outputs agree bit for bit."""
+    d = paged_case([300, 77, 5], [300, 1000, 40], 16, 2, dtype, seed=3)
+    dd = _dev(d)
+    rag = lib.attn_sink_prefill(dd["q"], dd["k"], dd["v"], dd["sinks"], dd["cu_seqlens_q"],
+                                dd["cu_seqlens_kv"], 300, d["group"], d["sm_scale"], True)
+    torch.cuda.synchronize()
+    assert torch.equal(run_paged(lib, d), rag.cpu())
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_paged_prefill_sink_extremes(lib, dtype):
+    """Sinks -inf, 0, moderate and +20 with logits up to about +-30."""
+    sinks = torch.tensor([-math.inf, 0.0, 1.3, 20.0, -math.inf, -2.0, 20.0, 0.5])
+    mults = [1.0, 2.0, 4.0, 7.5, 7.5, 4.0, 2.0, 1.0]
+    d = paged_case([77, 200], [500, 200], 8, 2, dtype, seed=4, sinks=sinks, q_head_mult=mults)
+    assert_close(run_paged(lib, d), oracle_paged(d), dtype, "paged sink extremes")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("splits", [1, 2, 5, 64])
+@pytest.mark.parametrize("causal", [True, False])
+def test_ragged_split_partials_and_merge(lib, dtype, splits, causal):
+    """Ragged split prefill: partial states against the oracle's, and the
+    merged result against the unsplit oracle."""
+    d = paged_case([3, 130, 1, 0, 64], [85, 130, 600, 5, 64], 8, 2, dtype, seed=splits)
+    got = run_ragged_partials(lib, d, causal, splits)
+    ref = oracle.prefill_partials(d["q"], d["k"], d["v"], d["sinks"], d["cu_seqlens_q"],
+                                  d["cu_seqlens_kv"], 2, 4, d["sm_scale"], causal, splits)
+    check_partials(got, ref, dtype, d["sinks"], "ragged S=%d" % splits)
+    merged = lib.attn_sink_merge(*(t.to(DEV) for t in got), out_dtype=dtype)
+    torch.cuda.synchronize()
+    full = oracle.prefill(d["q"], d["k"], d["v"], d["sinks"], d["cu_seqlens_q"],
+                          d["cu_seqlens_kv"], 2, 4, d["sm_scale"], causal)
+    assert_close(merged.cpu(), full, dtype, "ragged split merged")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("splits", [2, 7, 64])
+def test_paged_split_partials_and_merge(lib, dtype, splits):
+    d = paged_case([3, 130, 1, 0, 64], [85, 130, 600, 5, 64], 8, 2, dtype, seed=10 + splits)
+    got = run_paged(lib, d, True, splits)
+    ref = oracle_paged(d, True, splits)
+    check_partials(got, ref, dtype, d["sinks"], "paged S=%d" % splits)
+    merged = lib.attn_sink_merge(*(t.to(DEV) for t in got), out_dtype=dtype)
+    torch.cuda.synchronize()
+    assert_close(merged.cpu(), oracle_paged(d, True), dtype, "paged split merged")
+
+
+def test_split_empty_rows_keep_sink_in_chunk_zero(lib):
+    """More queries than keys: rows that see nothing hold (s, 1, 0) in chunk
+    0 and (-inf, 0, 0) elsewhere, and merge to 0."""
+    sinks = torch.tensor([1.25, -math.inf, 0.0, 20.0])
+    d = paged_case([6], [2], 4, 1, torch.bfloat16, seed=2, sinks=sinks)
+    pm, pd, po = run_ragged_partials(lib, d, True, 3)
+    for i in range(4):
+        for h in range(4):
+            s = float(sinks[h])
+            if s == -math.inf:
+                assert pm[i, h, 0] == -math.inf and pd[i, h, 0] == 0
+            else:
+                assert pd[i, h, 0] == 1 and abs(float(pm[i, h, 0]) - s) <= 1e-5 * max(1, abs(s))
+            assert torch.all(po[i, h, 0] == 0)
+            assert torch.all(pm[i, h, 1:] == -math.inf) and torch.all(pd[i, h, 1:] == 0)
+    merged = lib.attn_sink_merge(pm.to(DEV), pd.to(DEV), po.to(DEV))
+    torch.cuda.synchronize()
+    assert torch.all(merged.cpu()[:4] == 0)
+
+
+def test_paged_page_placement_and_poison_invariance(lib):
+    """Two physical placements with different junk in unused slots give the
+    same bits (unread slots never leak in, the tail of the last page
+    included)."""
+    d1 = paged_case([33, 100], [77, 500], 8, 2, torch.bfloat16, seed=5, fill=NAN)
+    d2 = dict(d1)
+    d2.update(workloads.pack_paged(d1["k"], d1["v"], d1["lens_kv"], seed=99, extra_pages=7,
+                                   fill=float("inf")))
+    a, b = run_paged(lib, d1), run_paged(lib, d2)
+    assert torch.all(torch.isfinite(a.float()))
+    assert torch.equal(a, b)
+
+
+def test_paged_prefill_deterministic(lib):
+    d = paged_case([200, 31], [900, 31], 16, 2, torch.bfloat16, seed=8)
+    assert torch.equal(run_paged(lib, d), run_paged(lib, d))
+    a = run_paged(lib, d, True, 5)
+    b = run_paged(lib, d, True, 5)
+    assert all(torch.equal(x, y) for x, y in zip(a, b))
+
+
+def test_chunked_prefill_long_cache_sampled(lib):
+    """Chunked prefill at serving size: 4 sequences, 512 new tokens each on
+    top of 15872 cached ones (kv_len 16384), Hq 64 / Hkv 8, bf16, split 8
+    ways and unsplit; sampled rows against the oracle."""
+    lens_q, lens_kv = [512] * 4, [16384] * 4
+    d = paged_case(lens_q, lens_kv, 64, 8, torch.bfloat16, seed=77, fill=0.0,
+                   sink_std=math.sqrt(2.0))
+    toks, heads = sample_prefill_rows(lens_q, 64, 24, seed=6)
+    ref = oracle_paged(d, True, rows=(toks, heads))
+    idx = (torch.as_tensor(toks), torch.as_tensor(heads).long())
+    out = run_paged(lib, d)
+    assert_close(out[idx], ref, torch.bfloat16, "chunked prefill unsplit")
+    pm, pd, po = run_paged(lib, d, True, 8)
+    merged = lib.attn_sink_merge(pm.to(DEV), pd.to(DEV), po.to(DEV))
+    torch.cuda.synchronize()
+    assert_close(merged.cpu()[idx], ref, torch.bfloat16, "chunked prefill split 8")
+    rm, rd, ro = oracle_paged(d, True, 8, rows=(toks, heads))
+    check_partials((pm[idx].unsqueeze(0), pd[idx].unsqueeze(0), po[idx].unsqueeze(0)),
+                   (rm[None], rd[None], ro[None]), torch.bfloat16, d["sinks"][heads][None],
+                   "chunked prefill partials")
