@@ -4,6 +4,9 @@ One step = one pass over every stage of the path on its synthetic workload:
   prefill  causal prefill, bf16, B=4 x 2048, Hq=64, Hkv=8, D=64      (MFMA-bound)
   decode   paged decode, bf16, B=64, kv_len U[512,8192], + merge     (HBM-bound)
   split    split-KV decode, bf16, B=4, kv_len 131072, 64 splits, + merge (HBM-bound)
+  paged    the prefill workload with keys and values in a paged cache
+  chunked  chunked prefill: B=1, 512 new tokens on a 32768-key paged cache,
+           unsplit, then split (default_prefill_splits: 4) + merge
 `value` is the prefill throughput in TFLOP/s (algorithmic flops: 4*D per
 causal-visible (query, key) pair) from HIP events around the prefill launch
 on the stream it runs on; the decode stages report achieved HBM GB/s.  The
@@ -133,37 +136,64 @@ def main():
         attn.attn_sink_prefill(c2["q"], c2["k"], c2["v"], c2["sinks"], c2["cu_seqlens_q"],
                                c2["cu_seqlens_kv"], 2048, 8, c2["sm_scale"], True, out=out2)
 
-    def run_decode(c, s, parts, out, ev=None):
+    def run_decode(c, s, parts):
         attn.attn_sink_decode_paged(c["q"], c["k_cache"], c["v_cache"], c["page_table"],
                                     c["kv_lens"], c["sinks"], 8, c["sm_scale"], s,
                                     partial_m=parts[0], partial_d=parts[1],
                                     partial_o=parts[2])
-        if ev is not None:
-            ev.record()
-        attn.attn_sink_merge(*parts, out=out)
 
-    names = ["prefill", "decode", "decode_merge", "split", "split_merge"]
+    # NEXT-row workloads: the prefill workload with its keys in a paged cache,
+    # and chunked prefill (few query tiles, long paged cache) unsplit and split.
+    pk2 = workloads.pack_paged(c2["k"], c2["v"], c2["lens_kv"], seed=2002)
+    out2p = torch.empty_like(c2["q"])
+    c6 = workloads.workload(6, device=dev)
+    s6 = attn.default_prefill_splits(1, 8, 8, 512, 32768)
+    out6 = torch.empty_like(c6["q"])
+    p6 = mk_partials(c6["q"].shape[0], s6)
+    o6 = torch.empty_like(c6["q"])
+
+    def run_paged_prefill():
+        attn.attn_sink_prefill_paged(c2["q"], pk2["k_cache"], pk2["v_cache"], pk2["page_table"],
+                                     c2["cu_seqlens_q"], pk2["kv_lens"], c2["sinks"], 2048, 8,
+                                     c2["sm_scale"], True, out=out2p)
+
+    def run_chunked(splits):
+        kw = dict(out=out6) if splits == 1 else dict(partial_m=p6[0], partial_d=p6[1],
+                                                     partial_o=p6[2])
+        attn.attn_sink_prefill_paged(c6["q"], c6["k_cache"], c6["v_cache"], c6["page_table"],
+                                     c6["cu_seqlens_q"], c6["kv_lens"], c6["sinks"], 512, 8,
+                                     c6["sm_scale"], True, num_splits=splits, **kw)
+
+    # One step, in launch order.  The kernel sequence of a step (ours only) is
+    # fixed, which is how profile summaries attribute dispatches to workloads.
+    ops = [
+        ("prefill", run_prefill),
+        ("_flush", flush.sum),
+        ("decode", lambda: run_decode(c3, s3, p3)),
+        ("decode_merge", lambda: attn.attn_sink_merge(*p3, out=o3)),
+        ("_flush", flush.sum),
+        ("split", lambda: run_decode(c4, s4, p4)),
+        ("split_merge", lambda: attn.attn_sink_merge(*p4, out=o4)),
+        ("paged_prefill", run_paged_prefill),
+        ("chunked", lambda: run_chunked(1)),
+        ("chunked_split", lambda: run_chunked(s6)),
+        ("chunked_merge", lambda: attn.attn_sink_merge(*p6, out=o6)),
+    ]
 
     def step(evs=None):
-        e = evs or {}
-        if evs: e["t0"].record()
-        run_prefill()
-        if evs: e["t1"].record()
-        flush.sum()
-        if evs: e["t2"].record()
-        run_decode(c3, s3, p3, o3, e.get("t3"))
-        if evs: e["t4"].record()
-        flush.sum()
-        if evs: e["t5"].record()
-        run_decode(c4, s4, p4, o4, e.get("t6"))
-        if evs: e["t7"].record()
+        for i, (_, fn) in enumerate(ops):
+            if evs:
+                evs[i].record()
+            fn()
+        if evs:
+            evs[len(ops)].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    evs = [{k: torch.cuda.Event(enable_timing=True) for k in
-            ("t0", "t1", "t2", "t3", "t4", "t5", "t6", "t7")} for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(ops) + 1)]
+           for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(args.steps):
@@ -171,12 +201,10 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
 
-    def avg_ms(a, b):
-        return sum(e[a].elapsed_time(e[b]) for e in evs) / len(evs)
-
-    t = dict(prefill=avg_ms("t0", "t1"), decode=avg_ms("t2", "t3"),
-             decode_merge=avg_ms("t3", "t4"), split=avg_ms("t5", "t6"),
-             split_merge=avg_ms("t6", "t7"))
+    t = {}
+    for i, (name, _) in enumerate(ops):
+        if not name.startswith("_"):
+            t[name] = sum(e[i].elapsed_time(e[i + 1]) for e in evs) / len(evs)
 
     fl2 = prefill_flops(c2["lens_q"], c2["lens_kv"], hq, 64)
     tflops = fl2 / (t["prefill"] * 1e-3) / 1e12
@@ -186,6 +214,12 @@ def main():
     gbs4 = b4["total"] / ((t["split"] + t["split_merge"]) * 1e-3) / 1e9
     gbs3_k = b3["decode"] / (t["decode"] * 1e-3) / 1e9
     gbs4_k = b4["decode"] / (t["split"] * 1e-3) / 1e9
+
+    fl2p = fl2
+    fl6 = prefill_flops(c6["lens_q"], c6["lens_kv"], hq, 64)
+    tf2p = fl2p / (t["paged_prefill"] * 1e-3) / 1e12
+    tf6 = fl6 / (t["chunked"] * 1e-3) / 1e12
+    tf6s = fl6 / ((t["chunked_split"] + t["chunked_merge"]) * 1e-3) / 1e12
 
     traffic = counted_traffic() or {}
     result = {
@@ -227,6 +261,22 @@ def main():
                          "decode_kernel_GB/s": round(gbs4_k, 1),
                          "decode_kernel_frac": round(gbs4_k / PEAK_HBM_GBS, 4),
                          "traffic": traffic.get("decode_split")},
+        "paged_prefill": {"workload": "causal prefill bf16 B=4 x 2048, Hq=64 Hkv=8 D=64, keys "
+                                      "and values from a paged cache (16-token pages, random "
+                                      "placement)",
+                          "us": round(t["paged_prefill"] * 1e3, 2),
+                          "TFLOP/s": round(tf2p, 2),
+                          "frac": round(tf2p / PEAK_BF16_TFLOPS, 4),
+                          "traffic": traffic.get("paged_prefill")},
+        "chunked_prefill": {"workload": c6["name"], "flops": fl6,
+                            "us_unsplit": round(t["chunked"] * 1e3, 2),
+                            "TFLOP/s_unsplit": round(tf6, 2),
+                            "frac_unsplit": round(tf6 / PEAK_BF16_TFLOPS, 4),
+                            "splits": s6,
+                            "us_split": round(t["chunked_split"] * 1e3, 2),
+                            "us_merge": round(t["chunked_merge"] * 1e3, 2),
+                            "TFLOP/s_split": round(tf6s, 2),
+                            "frac_split": round(tf6s / PEAK_BF16_TFLOPS, 4)},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(c2, args.cpu_seconds)

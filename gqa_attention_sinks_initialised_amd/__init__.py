@@ -305,3 +305,18 @@ def default_num_splits(kv_lens_host, num_kv_heads: int, cus: int = 256) -> int:
     s = max(1, -(-target // items))
     max_pages = max(1, max((int(L) + PAGE_SIZE - 1) // PAGE_SIZE for L in kv_lens_host))
     return int(min(s, max_pages, 256))
+
+
+def default_prefill_splits(batch: int, num_kv_heads: int, group_size: int, max_seqlen_q: int,
+                           max_seqlen_kv: int, cus: int = 256) -> int:
+    """Split count for prefill (attn_sink_prefill_partials / _paged): enough
+    workgroups for two per compute unit (the bf16 prefill kernel's
+    occupancy), each chunk keeping at least 256 keys so that the partial
+    states stay small next to the work.  Few query tiles over long key
+    ranges (chunked prefill) split; full prefill batches do not."""
+    tokens_per_wg = 4 * (64 // group_size)
+    wgs = -(-max_seqlen_q // tokens_per_wg) * batch * num_kv_heads
+    if wgs <= 0:
+        return 1
+    s = -(-2 * cus // wgs)
+    return int(max(1, min(s, max_seqlen_kv // 256)))

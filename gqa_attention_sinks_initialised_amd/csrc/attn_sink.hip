@@ -116,6 +116,12 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
+// Same with a wave-uniform part of the offset (held in an SGPR).
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                            uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
 // ============================================================ decode kernel
@@ -680,39 +686,57 @@ prefill_kernel(const PrefillArgs a) {
   u32x4 stk[NCH], stv[NCV][VREG];
   const uint32_t head_off = (uint32_t)kvh * kHeadDim * ES;
 
-  // Paged: a tile of 64 keys is 4 whole pages (chunks start on a page).  K
-  // chunk c of a tile is 16 bytes of key row c / CPR; V chunk c is 16 bytes
-  // of dim row (c % (16 CPR)) / ES of the dim-major V page; both lie in page
-  // (c / (16 CPR)) of the tile.  Each thread's page ids are fetched one tile
-  // ahead so that the data loads never wait for the page table.
+  // Paged: a tile of 64 keys is 4 whole pages (chunks start on a page).  A
+  // (page, kv head) block of either cache is 16 * 64 elements, contiguous,
+  // and chunk c of a tile is its 16-byte piece c % (16 CPR) -- a key row
+  // piece for K, a dim row piece for the dim-major V -- in page c / (16 CPR)
+  // of the tile.  A wave's 64 consecutive chunks share one page, so page ids
+  // and page base offsets are wave-uniform.  The ids are fetched one tile
+  // ahead with vector loads (which complete in order with the data loads, so
+  // no wait in the tile's compute is held up by them) and moved to scalar
+  // registers only when the next tile's loads are issued.
   static_assert(NCV == NCH, "K and V chunks of a tile must pair up");
-  int pid[NCH];
+  static_assert((kPage * CPR) % 64 == 0, "a wave's chunks must share a page");
+  const __amdgpu_buffer_rsrc_t ptr =
+      make_rsrc(PAGED ? a.page_table + (size_t)b * a.max_pages : nullptr,
+                PAGED ? (uint32_t)a.max_pages * 4u : 0u);
+  int pid_next[NCH];
+  auto page_of = [&](int jt, int u) {
+    return (c_lo + jt * BK) / kPage + (64 * w + NT * u) / (kPage * CPR);
+  };
   auto fetch_ids = [&](int jt) {
     if constexpr (PAGED) {
 #pragma unroll
-      for (int u = 0; u < NCH; ++u) {
-        const int lp = (c_lo + jt * BK) / kPage + (tid + NT * u) / (kPage * CPR);
-        const int id = (jt < n_tiles && lp * kPage < Lkv)
-                           ? a.page_table[(size_t)b * a.max_pages + lp] : -1;
-        pid[u] = (id >= 0 && id < a.num_pages) ? id : -1;  // bad ids: page skipped
-      }
+      for (int u = 0; u < NCH; ++u)
+        pid_next[u] = __builtin_amdgcn_raw_buffer_load_b32(ptr, 0, 4 * page_of(jt, u), 0);
     }
   };
 
   auto stage_load = [&](int jt) {
     const int key0 = c_lo + jt * BK;
     if constexpr (PAGED) {
+      constexpr uint32_t kBlock = kPage * kHeadDim * ES;  // one (page, kv head) block
+      // all ids to scalar registers first: the wait for them then comes
+      // before this tile's data loads are issued, not after
+      int ids[NCH];
+#pragma unroll
+      for (int u = 0; u < NCH; ++u) ids[u] = __builtin_amdgcn_readfirstlane(pid_next[u]);
 #pragma unroll
       for (int u = 0; u < NCH; ++u) {
         const int c = tid + NT * u;
-        const int key = c / CPR, part = c % CPR;
-        const int vrem = c % (kPage * CPR), dim = vrem / ES, vp = vrem % ES;
-        const int tp = c / (kPage * CPR);
-        if (c < BK * CPR && pid[u] >= 0) {
-          const uint32_t pg = (uint32_t)pid[u] * hkv + kvh;
-          stk[u] = buf_load16(kr, (pg * kPage + (key & (kPage - 1))) * (kHeadDim * ES) + part * 16);
-          const u32x4 x = buf_load16(vr, (pg * kHeadDim + dim) * (kPage * ES) + vp * 16);
-          stv[u][0] = keep_first(x, Lkv - (key0 + tp * kPage + vp * (16 / ES)), ES);
+        const int vrem = c % (kPage * CPR);
+        const int tp = (64 * w + NT * u) / (kPage * CPR);  // page of the tile (uniform)
+        const int id = ids[u];
+        // pages past the sequence and bad ids (outside [0, num_pages)) are skipped
+        if (page_of(jt, u) * kPage < Lkv && id >= 0 && id < a.num_pages) {
+          const uint32_t base = ((uint32_t)id * hkv + kvh) * kBlock;
+          stk[u] = buf_load16(kr, 16 * vrem, base);
+          stv[u][0] = buf_load16(vr, 16 * vrem, base);
+          // slots of the sequence's last page past its last key: zero V (their
+          // scores are masked, and 0 * junk must not reach O)
+          if (key0 + (tp + 1) * kPage > Lkv)
+            stv[u][0] = keep_first(stv[u][0], Lkv - (key0 + tp * kPage + (vrem % ES) * (16 / ES)),
+                                   ES);
         } else {
           stk[u] = u32x4{0, 0, 0, 0};
           stv[u][0] = u32x4{0, 0, 0, 0};
@@ -754,10 +778,14 @@ prefill_kernel(const PrefillArgs a) {
       }
     }
     if constexpr (PAGED) {
-      // V^T tile [64 dims][64 keys].  bf16: 128-byte rows of 4-key (8-byte)
-      // granules, granule g of dim row d at slot g ^ ((d >> 1) & 15), so the
-      // 32 dim rows one ds_read_b64 touches fall on distinct banks.  fp32:
-      // rows padded by 16 bytes.
+      // V^T tile [64 dims][64 keys].  bf16: a 128-byte dim row holds 8 pairs
+      // of 4-key granules; pair 2m + r (r = 0, 1) of the 16-key group m is
+      // granules 4m + r and 4m + r + 2, which is exactly what one lane's P.V
+      // operand needs, so it reads one 16-byte pair.  Pair p of row d sits
+      // at slot p ^ ((d >> 1) & 7): the 16 rows of a read phase hit distinct
+      // banks.  A staged chunk (8 keys of one dim row, page tp of the tile,
+      // half vp) fills half vp of pairs 2tp and 2tp + 1.  fp32: rows padded
+      // by 16 bytes.
 #pragma unroll
       for (int u = 0; u < NCV; ++u) {
         const int c = tid + NT * u;
@@ -766,9 +794,10 @@ prefill_kernel(const PrefillArgs a) {
         const int tp = c / (kPage * CPR);
         const u32x4 x = stv[u][0];
         if constexpr (DT == DT_BF16) {
-          const int gr = 4 * tp + 2 * vp, sw = (dim >> 1) & 15;
-          *reinterpret_cast<u32x2*>(vd + dim * 128 + 8 * (gr ^ sw)) = u32x2{x[0], x[1]};
-          *reinterpret_cast<u32x2*>(vd + dim * 128 + 8 * ((gr + 1) ^ sw)) = u32x2{x[2], x[3]};
+          const int sw = (dim >> 1) & 7;
+          char* row = vd + dim * 128 + 8 * vp;
+          *reinterpret_cast<u32x2*>(row + 16 * ((2 * tp) ^ sw)) = u32x2{x[0], x[1]};
+          *reinterpret_cast<u32x2*>(row + 16 * ((2 * tp + 1) ^ sw)) = u32x2{x[2], x[3]};
         } else {
           *reinterpret_cast<u32x4*>(vd + (dim * VROW + tp * kPage + 4 * vp) * ES) = x;
         }
@@ -910,8 +939,8 @@ prefill_kernel(const PrefillArgs a) {
       // source lane s of each 16-lane group points at V[kbase + s/4][dim0 +
       // 4*(s%4)]; after the transposing read lane i holds V[kbase + 0..3]
       // [dim0 + i] with dim0 + i = 32*db + lane%32
-      // (paged: the V^T tile is dim-major already; lane (g, col) reads the
-      // 4-key granules 8kb + 4hh + g and that + 2 of dim row 32db + col)
+      // (paged: the V^T tile is dim-major already; lane (g, col) reads pair
+      // 2(2kb + hh) + g of dim row 32db + col)
       typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
       const int sl = lane & 15;
 #pragma unroll
@@ -923,10 +952,9 @@ prefill_kernel(const PrefillArgs a) {
 #pragma unroll
           for (int db = 0; db < 2; ++db) {
             if constexpr (PAGED) {
-              const int dim = 32 * db + col, sw = (dim >> 1) & 15, g1 = 8 * kb + 4 * hh + g;
-              const u32x2 lo = *reinterpret_cast<const u32x2*>(vd + dim * 128 + 8 * (g1 ^ sw));
-              const u32x2 hi = *reinterpret_cast<const u32x2*>(vd + dim * 128 + 8 * ((g1 + 2) ^ sw));
-              vf[db] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+              const int dim = 32 * db + col, pr = 2 * (2 * kb + hh) + g;
+              vf[db] = *reinterpret_cast<const u32x4*>(vd + dim * 128 +
+                                                       16 * (pr ^ ((dim >> 1) & 7)));
               continue;
             }
             const int dim = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (sl & 3);

@@ -1,0 +1,24 @@
+"""Host-side planning logic of the binding (CPU only, no GPU call)."""
+import gqa_attention_sinks_initialised_amd as m
+
+
+def test_decode_splits_fill_the_gpu():
+    # 64 sequences x 8 kv heads = 512 items: 4 splits give 2048 = 8 per CU
+    assert m.default_num_splits([4096] * 64, 8) == 4
+    # few long sequences split up to the 256 cap
+    assert m.default_num_splits([131072] * 4, 8) == 64
+    # never more splits than pages
+    assert m.default_num_splits([20], 1) == 2
+    assert m.default_num_splits([], 8) == 1
+
+
+def test_prefill_splits():
+    # chunked prefill: 512 tokens of one sequence, G = 8 -> 32 tokens per
+    # workgroup, 16 tiles x 8 kv heads = 128 workgroups -> 4 splits
+    assert m.default_prefill_splits(1, 8, 8, 512, 32768) == 4
+    # a full prefill batch already fills the GPU
+    assert m.default_prefill_splits(4, 8, 8, 2048, 2048) == 1
+    # short key ranges are not cut below 256 keys per chunk
+    assert m.default_prefill_splits(1, 1, 8, 16, 600) == 2
+    assert m.default_prefill_splits(1, 1, 8, 16, 100) == 1
+    assert m.default_prefill_splits(0, 8, 8, 0, 0) == 1

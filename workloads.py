@@ -15,7 +15,7 @@ Layouts (shared by every caller):
   paged prefill:   q [total_q, Hq, D] with cu_seqlens_q, and the paged cache
                    of decode (pack_paged lays ragged k / v out that way)
 
-The five named workloads follow the benchmark configurations of the project:
+The named workloads follow the benchmark configurations of the project:
   1  tiny causal prefill, fp32: B=1, L=128, Hq=8, Hkv=2, D=64
   2  causal prefill, bf16: B=4 x 2048, Hq=64, Hkv=8, D=64
   3  paged decode, bf16: B=64, kv_len ~ U{512..8192}, 16-token pages
@@ -23,6 +23,8 @@ The five named workloads follow the benchmark configurations of the project:
   5  ragged causal prefill with numeric edge cases, bf16: 16 sequences,
      len ~ U{128..4096}, sinks from {-inf, 0, N(0,1), +20}, Q multipliers
      {1, 2, 4, 7.5} so that logits reach about +-30
+  6  chunked prefill against the paged cache, bf16: B=1, 512 new query
+     tokens, kv_len 32768 (the new tokens' keys included), Hq=64, Hkv=8
 Seeds are 1000 + workload number.
 """
 from __future__ import annotations
@@ -170,7 +172,7 @@ def c5_sinks_and_mults(hq, seed):
 
 
 def workload(n: int, device="cpu", cache_device=None) -> dict:
-    """The named workloads 1..5 (see module docstring)."""
+    """The named workloads 1..6 (see module docstring)."""
     seed = SEED_BASE + n
     if n == 1:
         d = prefill_inputs([128], hq=8, hkv=2, dtype=torch.float32, seed=seed,
@@ -212,4 +214,12 @@ def workload(n: int, device="cpu", cache_device=None) -> dict:
                  name="ragged causal prefill bf16 16 seqs len U[128,4096] Hq=64 "
                       "Hkv=8 D=64, edge-case sinks and logits")
         return d
-    raise ValueError("workload number must be 1..5")
+    if n == 6:
+        d = prefill_inputs([512], [32768], hq=64, hkv=8, dtype=torch.bfloat16, seed=seed,
+                           sink_std=math.sqrt(2.0), device=device)
+        d.update(pack_paged(d["k"], d["v"], d["lens_kv"], seed=seed + 1))
+        d.update(kind="prefill_paged", causal=True,
+                 name="chunked prefill bf16 B=1, 512 new tokens on a paged cache of 32768 "
+                      "keys, Hq=64 Hkv=8 D=64 page 16")
+        return d
+    raise ValueError("workload number must be 1..6")
