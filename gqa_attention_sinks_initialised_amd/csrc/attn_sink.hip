@@ -50,9 +50,13 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr int kHeadDim = 64;
 constexpr int kPage = 16;
-// Prefill keeps a stale reference max until a row's max grows by more than
-// this many log2 units, so probabilities stay below 2^8 between rescales.
-constexpr float kRescaleLog2 = 8.0f;
+// Prefill forms P against a lazily kept reference and moves the reference
+// only when a lane's share of a tile's row sum exceeds this bound (P then
+// stays below 2^16, far from fp32 / bf16 overflow).
+#ifndef ATTN_SINK_LANE_SUM_MAX
+#define ATTN_SINK_LANE_SUM_MAX 65536.0f
+#endif
+constexpr float kLaneSumMax = ATTN_SINK_LANE_SUM_MAX;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -659,7 +663,9 @@ prefill_kernel(const PrefillArgs a) {
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const float s = (valid[rb] && split == 0) ? sinks[head[rb]] : kNegInf;
-    m_run[rb] = s * kLog2e;
+    // rows past the tile's tokens get a finite reference: their (unused) P
+    // then never asks for the slow path
+    m_run[rb] = valid[rb] ? s * kLog2e : 0.f;
     d_run[rb] = (g == 0 && s != kNegInf) ? 1.f : 0.f;
   }
   f32x16 acc_o[2][RB];
@@ -865,12 +871,17 @@ prefill_kernel(const PrefillArgs a) {
       }
     }
 
-    // Online softmax.  The reference max m_run is raised only when a row's
-    // tile max exceeds it by more than kRescaleLog2 (then only that row's O
-    // and d are rescaled, in a wave-uniform, rarely taken branch); otherwise
-    // p = 2^(x - m_run) stays below 2^kRescaleLog2.  O/d does not depend on
-    // which reference is used.
-    u32x4 pf[RB][2][2];  // bf16 P^T operands [rb][kb][half]
+    // Online softmax against a lazily kept reference m_run (log2 units) that
+    // starts at the sink.  P = 2^(x - m_run) is formed directly, with no row
+    // max per tile: the reference only has to keep P finite and bounded, and
+    // O/d does not depend on which reference is used.  A row takes the slow
+    // path -- true max of the tile, rescale of its O and d, P formed again --
+    // when it has no reference yet (m_run = -inf) or when a lane's share of
+    // the tile's row sum exceeds kLaneSumMax = 2^16 (which also catches an
+    // infinite P).  The branch is wave-uniform, but only the rows that need
+    // it change, so a row's result never depends on other rows.
+    u32x4 pf[RB][2][2];   // bf16 P^T operands [rb][kb][half]
+    float pt[RB][2][16];  // fp32 P^T
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       if constexpr (decltype(masked)::value) {
@@ -884,53 +895,63 @@ prefill_kernel(const PrefillArgs a) {
             sacc[kb][rb][r] = (8 * (r >> 2) + (r & 3) > thr) ? kNegInf : sacc[kb][rb][r];
         }
       }
-      float mx4[4] = {kNegInf, kNegInf, kNegInf, kNegInf};  // 4 chains of max3
+      // P of this row block against reference m; returns the lane's row sum
+      auto form_p = [&](float m) {
+        const float m_use = (m == kNegInf) ? 0.f : m;
+        float ps[4] = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (DT == DT_BF16) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+          for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          float& a = mx4[(kb * 8 + r / 2) & 3];
-          a = fmaxf(fmaxf(a, sacc[kb][rb][r]), sacc[kb][rb][r + 1]);
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int r = 8 * hh + 2 * e;
+                const float p0 = fast_exp2(__builtin_fmaf(sacc[kb][rb][r], qk_scale_log2, -m_use));
+                const float p1 =
+                    fast_exp2(__builtin_fmaf(sacc[kb][rb][r + 1], qk_scale_log2, -m_use));
+                const unsigned int pk = pack_bf16x2(p0, p1);
+                pf[rb][kb][hh][e] = pk;
+                ps[e] = add_bf16x2(pk, ps[e]);
+              }
+        } else {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const float pr = fast_exp2(__builtin_fmaf(sacc[kb][rb][r], qk_scale_log2, -m_use));
+              pt[rb][kb][r] = pr;
+              ps[r & 3] += pr;
+            }
         }
-      const float mx =
-          xor_max(fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3])), 32) * qk_scale_log2;
-      const bool grow = mx > m_run[rb] + kRescaleLog2;
-      if (wave_any(grow)) {
-        // only rows that crossed the threshold move their reference (others
-        // scale by exactly 1), so a row's result never depends on other rows
-        const float alpha = grow ? fast_exp2(m_run[rb] - mx) : 1.f;
+        return (ps[0] + ps[1]) + (ps[2] + ps[3]);
+      };
+      float rs = form_p(m_run[rb]);
+      const bool slow = !(rs <= kLaneSumMax) || m_run[rb] == kNegInf;
+      if (wave_any(slow)) {
+        // rows (both lanes) that need a new reference move it to the max of
+        // their reference and this tile's logits; the others keep theirs and
+        // form bit-identical P again
+        const bool need = xor_max(slow ? 1.f : 0.f, 32) > 0.f;
+        float mx4[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; r += 2) {
+            float& a = mx4[(kb * 8 + r / 2) & 3];
+            a = fmaxf(fmaxf(a, sacc[kb][rb][r]), sacc[kb][rb][r + 1]);
+          }
+        const float mx =
+            xor_max(fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3])), 32) * qk_scale_log2;
+        const float m_new = need ? fmaxf(m_run[rb], mx) : m_run[rb];
+        const float alpha = (m_new == m_run[rb]) ? 1.f : fast_exp2(m_run[rb] - m_new);
         d_run[rb] *= alpha;
 #pragma unroll
         for (int db = 0; db < 2; ++db) acc_o[db][rb] *= alpha;
-        m_run[rb] = grow ? mx : m_run[rb];
+        m_run[rb] = m_new;
+        rs = form_p(m_new);
       }
-      const float m_use = (m_run[rb] == kNegInf) ? 0.f : m_run[rb];
-      float ps[4] = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (DT == DT_BF16) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = 8 * hh + 2 * e;
-              const float p0 = fast_exp2(__builtin_fmaf(sacc[kb][rb][r], qk_scale_log2, -m_use));
-              const float p1 = fast_exp2(__builtin_fmaf(sacc[kb][rb][r + 1], qk_scale_log2, -m_use));
-              const unsigned int pk = pack_bf16x2(p0, p1);
-              pf[rb][kb][hh][e] = pk;
-              ps[e] = add_bf16x2(pk, ps[e]);
-            }
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float pr = fast_exp2(__builtin_fmaf(sacc[kb][rb][r], qk_scale_log2, -m_use));
-            sacc[kb][rb][r] = pr;
-            ps[r & 3] += pr;
-          }
-      }
-      d_run[rb] += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+      d_run[rb] += rs;
     }
 
     // O^T += V^T P^T.  bf16: key step outermost, both dim blocks' V^T
@@ -989,7 +1010,7 @@ prefill_kernel(const PrefillArgs a) {
 #pragma unroll
               for (int rb = 0; rb < RB; ++rb)
                 acc_o[db][rb] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                    __uint_as_float(vf[e]), sacc[kb][rb][4 * qd + e], acc_o[db][rb], 0, 0, 0);
+                    __uint_as_float(vf[e]), pt[rb][kb][4 * qd + e], acc_o[db][rb], 0, 0, 0);
           }
       }
     }
