@@ -51,10 +51,16 @@ constexpr float kNegInf = -__builtin_huge_valf();
 constexpr int kHeadDim = 64;
 constexpr int kPage = 16;
 // Prefill forms P against a lazily kept reference and moves the reference
-// only when a lane's share of a tile's row sum exceeds this bound (P then
-// stays below 2^16, far from fp32 / bf16 overflow).
+// only when a lane's share of a tile's row sum exceeds this bound: P then
+// stays below 2^64, so O and d (sums of P times values, up to 2^17 keys)
+// stay far below the fp32 and bf16 range (2^128).
+// Order the LDS operand reads of each MFMA step ahead of the previous
+// step's MFMAs (scheduling hints).
+#ifndef ATTN_SINK_PIPE_ORDER
+#define ATTN_SINK_PIPE_ORDER 1
+#endif
 #ifndef ATTN_SINK_LANE_SUM_MAX
-#define ATTN_SINK_LANE_SUM_MAX 65536.0f
+#define ATTN_SINK_LANE_SUM_MAX 0x1p64f
 #endif
 constexpr float kLaneSumMax = ATTN_SINK_LANE_SUM_MAX;
 
@@ -840,20 +846,38 @@ prefill_kernel(const PrefillArgs a) {
     // S^T = K Q^T.  bf16: k-step outermost so that the 2*RB accumulators
     // are interleaved and consecutive MFMAs never depend on each other.
     if constexpr (DT == DT_BF16) {
+      // the K operands of k-step s + 1 are read before the MFMAs of step s
+      auto k_operand = [&](int s, int kb) {
+        const int krw = kb * 32 + col;
+        return *reinterpret_cast<const u32x4*>(kd + krw * 128 + 16 * ((4 * g + s) ^ (krw & 7)));
+      };
+      u32x4 kf[2][2];
+      kf[0][0] = k_operand(0, 0);
+      kf[0][1] = k_operand(0, 1);
 #pragma unroll
       for (int s = 0; s < QV; ++s) {
+        if (s + 1 < QV) {
+          kf[(s + 1) & 1][0] = k_operand(s + 1, 0);
+          kf[(s + 1) & 1][1] = k_operand(s + 1, 1);
+        }
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const int krw = kb * 32 + col;
-          const u32x4 kf =
-              *reinterpret_cast<const u32x4*>(kd + krw * 128 + 16 * ((4 * g + s) ^ (krw & 7)));
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb)
             sacc[kb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8, kf), __builtin_bit_cast(bf16x8, qf[rb][s]),
+                __builtin_bit_cast(bf16x8, kf[s & 1][kb]), __builtin_bit_cast(bf16x8, qf[rb][s]),
                 sacc[kb][rb], 0, 0, 0);
-        }
       }
+#if ATTN_SINK_PIPE_ORDER
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+#endif
     } else {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -877,7 +901,7 @@ prefill_kernel(const PrefillArgs a) {
     // O/d does not depend on which reference is used.  A row takes the slow
     // path -- true max of the tile, rescale of its O and d, P formed again --
     // when it has no reference yet (m_run = -inf) or when a lane's share of
-    // the tile's row sum exceeds kLaneSumMax = 2^16 (which also catches an
+    // the tile's row sum exceeds kLaneSumMax (which also catches an
     // infinite P).  The branch is wave-uniform, but only the rows that need
     // it change, so a row's result never depends on other rows.
     u32x4 pf[RB][2][2];   // bf16 P^T operands [rb][kb][half]
@@ -964,37 +988,51 @@ prefill_kernel(const PrefillArgs a) {
       // 2(2kb + hh) + g of dim row 32db + col)
       typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
       const int sl = lane & 15;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
+      // V^T operand of dim block db for key step (kb, hh)
+      auto v_operand = [&](int kb, int hh, int db) {
+        if constexpr (PAGED) {
+          const int dim = 32 * db + col, pr = 2 * (2 * kb + hh) + g;
+          return *reinterpret_cast<const u32x4*>(vd + dim * 128 + 16 * (pr ^ ((dim >> 1) & 7)));
+        } else {
           const int r0 = kb * 32 + 16 * hh + 4 * g + (sl >> 2), r1 = r0 + 8;
-          u32x4 vf[2];
-#pragma unroll
-          for (int db = 0; db < 2; ++db) {
-            if constexpr (PAGED) {
-              const int dim = 32 * db + col, pr = 2 * (2 * kb + hh) + g;
-              vf[db] = *reinterpret_cast<const u32x4*>(vd + dim * 128 +
-                                                       16 * (pr ^ ((dim >> 1) & 7)));
-              continue;
-            }
-            const int dim = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (sl & 3);
-            const int chunk = dim >> 3, sub = 2 * (dim & 7);
-            const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_i16x4*)(vd + r0 * 128 + 16 * (chunk ^ (2 * (r0 & 3))) + sub));
-            const i16x4 c = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_i16x4*)(vd + r1 * 128 + 16 * (chunk ^ (2 * (r1 & 3))) + sub));
-            const u32x2 lo = __builtin_bit_cast(u32x2, a), hi = __builtin_bit_cast(u32x2, c);
-            vf[db] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-          }
-#pragma unroll
-          for (int db = 0; db < 2; ++db)
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb)
-              acc_o[db][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                  __builtin_bit_cast(bf16x8, vf[db]), __builtin_bit_cast(bf16x8, pf[rb][kb][hh]),
-                  acc_o[db][rb], 0, 0, 0);
+          const int dim = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (sl & 3);
+          const int chunk = dim >> 3, sub = 2 * (dim & 7);
+          const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4*)(vd + r0 * 128 + 16 * (chunk ^ (2 * (r0 & 3))) + sub));
+          const i16x4 c = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4*)(vd + r1 * 128 + 16 * (chunk ^ (2 * (r1 & 3))) + sub));
+          const u32x2 lo = __builtin_bit_cast(u32x2, a), hi = __builtin_bit_cast(u32x2, c);
+          return u32x4{lo[0], lo[1], hi[0], hi[1]};
         }
+      };
+      // the operands of key step t + 1 are read before the MFMAs of step t
+      u32x4 vf[2][2];
+      vf[0][0] = v_operand(0, 0, 0);
+      vf[0][1] = v_operand(0, 0, 1);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        if (t + 1 < 4) {
+          vf[(t + 1) & 1][0] = v_operand((t + 1) >> 1, (t + 1) & 1, 0);
+          vf[(t + 1) & 1][1] = v_operand((t + 1) >> 1, (t + 1) & 1, 1);
+        }
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb)
+            acc_o[db][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, vf[t & 1][db]),
+                __builtin_bit_cast(bf16x8, pf[rb][t >> 1][t & 1]), acc_o[db][rb], 0, 0, 0);
+      }
+#if ATTN_SINK_PIPE_ORDER
+      __builtin_amdgcn_sched_group_barrier(0x100, PAGED ? 2 : 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, PAGED ? 2 : 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, PAGED ? 2 : 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, PAGED ? 2 : 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+#endif
     } else {
 #pragma unroll
       for (int db = 0; db < 2; ++db) {
