@@ -97,11 +97,6 @@ __device__ __forceinline__ unsigned int pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(unsigned int, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
-// acc + lo + hi of a packed bf16 pair (v_dot2_f32_bf16 against (1, 1)).
-__device__ __forceinline__ float add_bf16x2(unsigned int pk, float acc) {
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones, acc, false);
-}
 
 // True on every lane if the predicate holds on any lane of the wave.
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
@@ -934,9 +929,10 @@ prefill_kernel(const PrefillArgs a) {
                 const float p0 = fast_exp2(__builtin_fmaf(sacc[kb][rb][r], qk_scale_log2, -m_use));
                 const float p1 =
                     fast_exp2(__builtin_fmaf(sacc[kb][rb][r + 1], qk_scale_log2, -m_use));
-                const unsigned int pk = pack_bf16x2(p0, p1);
-                pf[rb][kb][hh][e] = pk;
-                ps[e] = add_bf16x2(pk, ps[e]);
+                pf[rb][kb][hh][e] = pack_bf16x2(p0, p1);
+                // the row sum adds the fp32 P: v_dot2 on the packed pair would
+                // issue to the matrix pipe and stall beside the MFMAs
+                ps[e] += p0 + p1;
               }
         } else {
 #pragma unroll
