@@ -59,6 +59,10 @@ constexpr int kPage = 16;
 #ifndef ATTN_SINK_PIPE_ORDER
 #define ATTN_SINK_PIPE_ORDER 1
 #endif
+// Paged decode: load bf16 K pages as whole rows and re-deal them in LDS.
+#ifndef ATTN_SINK_DECODE_KLDS
+#define ATTN_SINK_DECODE_KLDS 1
+#endif
 #ifndef ATTN_SINK_LANE_SUM_MAX
 #define ATTN_SINK_LANE_SUM_MAX 0x1p64f
 #endif
@@ -109,6 +113,13 @@ __device__ __forceinline__ V ld_global(const void* p) {
   return *reinterpret_cast<const V*>(p);
 }
 
+// Load marked non-temporal: data read once (the paged decode's K and V) is
+// streamed past the caches, which reads random 2 KB pages ~10% faster.
+template <typename V>
+__device__ __forceinline__ V ld_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const V*>(p));
+}
+
 // Raw buffer resource over [base, base + bytes): loads past the end return
 // zero and stores past the end are dropped, which is how ragged sequence
 // tails are handled without branches.
@@ -155,8 +166,13 @@ struct DecodeFrag<DT_F32> {
   u32x4 v[4];  // Vt[16j + l%16][4g .. 4g+3]
 };
 
+// Four bf16 decode waves per SIMD (at most 128 VGPRs): four workgroups per
+// compute unit keep more pages in flight.
+#ifndef ATTN_SINK_DECODE_MIN_WAVES
+#define ATTN_SINK_DECODE_MIN_WAVES 4
+#endif
 template <int DT, int WAVES, int UNROLL>
-__global__ __launch_bounds__(64 * WAVES) void decode_kernel(
+__global__ __launch_bounds__(64 * WAVES, (DT == DT_BF16 ? ATTN_SINK_DECODE_MIN_WAVES : 1)) void decode_kernel(
     const char* __restrict__ q, const char* __restrict__ kc, const char* __restrict__ vc,
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ kv_lens,
     const float* __restrict__ sinks, int max_pages, int num_pages, int hkv, int group,
@@ -170,7 +186,9 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(
   // for up to 64 sequences blockIdx.z is read as a rank and mapped to the
   // sequence with the rank-th largest kv_len (ties by index).  Each wave
   // ranks the 64 lengths with one compare per lane and step.
-  int b = blockIdx.z;
+  // The rank search leaves every length in a register, so the sequence's own
+  // length costs no second dependent load.
+  int b = blockIdx.z, L;
   const int batch = gridDim.z;
   if (batch <= 64) {
     const int li = lane < batch ? clampi(kv_lens[lane], 0, max_pages * kPage) : -1;
@@ -181,6 +199,9 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(
     }
     const uint64_t hit = __builtin_amdgcn_ballot_w64(lane < batch && rank == (int)blockIdx.z);
     b = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(hit));
+    L = __builtin_amdgcn_readlane(li, b);
+  } else {
+    L = clampi(kv_lens[b], 0, max_pages * kPage);
   }
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, g = lane >> 4;
@@ -188,7 +209,6 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(
   const bool head_ok = n < group;
   const int h = kvh * group + (head_ok ? n : 0);
 
-  const int L = clampi(kv_lens[b], 0, max_pages * kPage);
   const int np = (L + kPage - 1) / kPage;
   const int ppc = (np + splits - 1) / splits;
   const int p_begin = min(c * ppc, np);
@@ -221,23 +241,36 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(
   const int32_t* pt = page_table + (size_t)b * max_pages;
   const size_t head_page_stride = kPageElems * ES;  // bytes per (page, kv head)
 
+#if ATTN_SINK_DECODE_KLDS
+  // bf16 K arrives as whole 128-byte token rows (load s, lane i: token
+  // 8s + i/8, 16-byte chunk i%8) and is re-dealt into the MFMA operand
+  // layout through a 2 KB LDS block per wave.  Chunk c of token t sits in
+  // slot 8t + (c ^ ((t >> 1) & 7)), so the 16 lanes of each operand read
+  // (tokens 0..15, one chunk) hit 16 different bank groups.
+  __shared__ u32x4 k_lds[DT == DT_BF16 ? WAVES : 1][128];
+  auto k_slot = [](int t, int ch) { return 8 * t + (ch ^ ((t >> 1) & 7)); };
+#endif
   auto load_page = [&](int phys, DecodeFrag<DT>& f) {
     const char* kp = kc + ((size_t)phys * hkv + kvh) * head_page_stride;
     const char* vp = vc + ((size_t)phys * hkv + kvh) * head_page_stride;
     if constexpr (DT == DT_BF16) {
 #pragma unroll
       for (int s = 0; s < 2; ++s)
-        f.k[s] = ld_global<u32x4>(kp + ((size_t)n * kHeadDim + 32 * s + 8 * g) * ES);
+#if ATTN_SINK_DECODE_KLDS
+        f.k[s] = ld_stream<u32x4>(kp + 1024 * s + 16 * lane);
+#else
+        f.k[s] = ld_stream<u32x4>(kp + ((size_t)n * kHeadDim + 32 * s + 8 * g) * ES);
+#endif
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        f.v[j] = ld_global<u32x2>(vp + ((size_t)(16 * j + n) * kPage + 4 * g) * ES);
+        f.v[j] = ld_stream<u32x2>(vp + ((size_t)(16 * j + n) * kPage + 4 * g) * ES);
     } else {
 #pragma unroll
       for (int s = 0; s < 4; ++s)
-        f.k[s] = ld_global<u32x4>(kp + ((size_t)n * kHeadDim + 16 * g + 4 * s) * ES);
+        f.k[s] = ld_stream<u32x4>(kp + ((size_t)n * kHeadDim + 16 * g + 4 * s) * ES);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        f.v[j] = ld_global<u32x4>(vp + ((size_t)(16 * j + n) * kPage + 4 * g) * ES);
+        f.v[j] = ld_stream<u32x4>(vp + ((size_t)(16 * j + n) * kPage + 4 * g) * ES);
     }
   };
 
@@ -245,6 +278,18 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(
     // S^T tile
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
     if constexpr (DT == DT_BF16) {
+#if ATTN_SINK_DECODE_KLDS
+      // LDS operations of one wave run in order, so wavefront-scope fences
+      // (compiler ordering only) make the re-deal safe without waits.
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+#pragma unroll
+      for (int t = 0; t < 2; ++t) k_lds[w][k_slot(8 * t + (lane >> 3), lane & 7)] = f.k[t];
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int t = 0; t < 2; ++t) f.k[t] = k_lds[w][k_slot(n, 4 * t + g)];
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#endif
 #pragma unroll
       for (int t = 0; t < 2; ++t)
         s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, f.k[t]),
