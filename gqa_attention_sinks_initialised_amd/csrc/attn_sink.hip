@@ -16,11 +16,11 @@
 //                   workgroup owns (sequence, kv head, key chunk); the G query
 //                   heads of the group sit in the 16 columns of one MFMA tile,
 //                   so every K and V page is loaded from HBM once for all of
-//                   them.  K and V fragments go straight from HBM into MFMA
-//                   operands (no LDS staging); pages are read with 16-byte
-//                   (K) and 8-byte (V) vector loads.  The V page is stored
-//                   dim-major so that the P.V contraction (over tokens) reads
-//                   contiguous memory.
+//                   them.  Pages are read with non-temporal vector loads: V
+//                   (stored dim-major, so that the P.V contraction over
+//                   tokens reads contiguous memory) straight into MFMA
+//                   operands, K as whole 128-byte rows re-dealt into the
+//                   operand layout through 2 KB of LDS per wave.
 //   merge_kernel    split-KV merge of (m, d, o) partial states.
 //   prefill_kernel  ragged (causal) prefill.  One workgroup owns a tile of
 //                   query tokens x all G heads of one kv head (4 waves x 64
@@ -54,19 +54,7 @@ constexpr int kPage = 16;
 // only when a lane's share of a tile's row sum exceeds this bound: P then
 // stays below 2^64, so O and d (sums of P times values, up to 2^17 keys)
 // stay far below the fp32 and bf16 range (2^128).
-// Order the LDS operand reads of each MFMA step ahead of the previous
-// step's MFMAs (scheduling hints).
-#ifndef ATTN_SINK_PIPE_ORDER
-#define ATTN_SINK_PIPE_ORDER 1
-#endif
-// Paged decode: load bf16 K pages as whole rows and re-deal them in LDS.
-#ifndef ATTN_SINK_DECODE_KLDS
-#define ATTN_SINK_DECODE_KLDS 1
-#endif
-#ifndef ATTN_SINK_LANE_SUM_MAX
-#define ATTN_SINK_LANE_SUM_MAX 0x1p64f
-#endif
-constexpr float kLaneSumMax = ATTN_SINK_LANE_SUM_MAX;
+constexpr float kLaneSumMax = 0x1p64f;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -140,6 +128,44 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t v
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
+// Buffer resource words over [base, base + bytes) (the same descriptor as
+// make_rsrc), for the loads issued from inline assembly below.
+__device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, 0x00020000u};
+}
+
+// 16 bytes per lane from a buffer straight into LDS: lane i writes
+// [lds + 16 i, +16) (lds wave-uniform); offsets past the buffer read zero.
+// Issued from inline assembly so that the compiler's wait insertion, which
+// would wait for every such load before any LDS read, does not see it: the
+// caller waits for these loads itself (vmcnt; loads complete in order).  The
+// LDS address goes in M0, which is saved and restored around the load, with
+// the one wait state gfx9 needs between an SALU write of M0 and its read.
+__device__ __forceinline__ void load_to_lds16(u32x4 rsrc, uint32_t voff, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(rsrc), "s"(lds)
+      : "memory");
+}
+
+// Workgroup barrier ordering LDS only (global loads in flight stay in flight).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
 // ============================================================ decode kernel
 //
 // Work item = (key chunk c, kv head, sequence b); WAVES waves share it by
@@ -156,7 +182,7 @@ struct DecodeFrag;
 
 template <>
 struct DecodeFrag<DT_BF16> {
-  u32x4 k[2];  // K[token l%16][32s + 8g .. +7], s = 0, 1
+  u32x4 k[2];  // as loaded: K[token 8s + l/8][8(l%8) .. +7], s = 0, 1
   u32x2 v[4];  // Vt[16j + l%16][4g .. 4g+3], j = 0..3
 };
 
@@ -241,7 +267,6 @@ __global__ __launch_bounds__(64 * WAVES, (DT == DT_BF16 ? ATTN_SINK_DECODE_MIN_W
   const int32_t* pt = page_table + (size_t)b * max_pages;
   const size_t head_page_stride = kPageElems * ES;  // bytes per (page, kv head)
 
-#if ATTN_SINK_DECODE_KLDS
   // bf16 K arrives as whole 128-byte token rows (load s, lane i: token
   // 8s + i/8, 16-byte chunk i%8) and is re-dealt into the MFMA operand
   // layout through a 2 KB LDS block per wave.  Chunk c of token t sits in
@@ -249,18 +274,13 @@ __global__ __launch_bounds__(64 * WAVES, (DT == DT_BF16 ? ATTN_SINK_DECODE_MIN_W
   // (tokens 0..15, one chunk) hit 16 different bank groups.
   __shared__ u32x4 k_lds[DT == DT_BF16 ? WAVES : 1][128];
   auto k_slot = [](int t, int ch) { return 8 * t + (ch ^ ((t >> 1) & 7)); };
-#endif
   auto load_page = [&](int phys, DecodeFrag<DT>& f) {
     const char* kp = kc + ((size_t)phys * hkv + kvh) * head_page_stride;
     const char* vp = vc + ((size_t)phys * hkv + kvh) * head_page_stride;
     if constexpr (DT == DT_BF16) {
 #pragma unroll
       for (int s = 0; s < 2; ++s)
-#if ATTN_SINK_DECODE_KLDS
         f.k[s] = ld_stream<u32x4>(kp + 1024 * s + 16 * lane);
-#else
-        f.k[s] = ld_stream<u32x4>(kp + ((size_t)n * kHeadDim + 32 * s + 8 * g) * ES);
-#endif
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         f.v[j] = ld_stream<u32x2>(vp + ((size_t)(16 * j + n) * kPage + 4 * g) * ES);
@@ -278,7 +298,6 @@ __global__ __launch_bounds__(64 * WAVES, (DT == DT_BF16 ? ATTN_SINK_DECODE_MIN_W
     // S^T tile
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
     if constexpr (DT == DT_BF16) {
-#if ATTN_SINK_DECODE_KLDS
       // LDS operations of one wave run in order, so wavefront-scope fences
       // (compiler ordering only) make the re-deal safe without waits.
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -289,7 +308,6 @@ __global__ __launch_bounds__(64 * WAVES, (DT == DT_BF16 ? ATTN_SINK_DECODE_MIN_W
 #pragma unroll
       for (int t = 0; t < 2; ++t) f.k[t] = k_lds[w][k_slot(n, 4 * t + g)];
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#endif
 #pragma unroll
       for (int t = 0; t < 2; ++t)
         s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, f.k[t]),
@@ -544,9 +562,10 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pm
 // Workgroup = WAVES waves; wave w owns ROWS = 32*RB rows, row r = (token
 // r / G, head r % G) of tokens [t_begin + w*TW, +TW), TW = ROWS / G, so every
 // query head of a kv group reads the same K/V tile.  Key tiles of 64 are
-// staged in LDS (K row-major, V transposed to dim-major) with a double
-// buffer: the next tile's global loads are in flight while the current tile
-// is used.  Per tile and wave:
+// staged in LDS: bf16 ragged K/V go from global memory straight into a
+// three-stage ring, two tiles ahead of the one in use; paged and fp32 tiles
+// pass through registers into a double buffer, one tile ahead.  Per tile
+// and wave:
 //   S^T[64 keys x ROWS]  = K . Q^T       (2 key blocks x RB row blocks)
 //   O^T[64 dims x ROWS] += V^T . P^T     (2 dim blocks x RB row blocks)
 // A 32x32 MFMA result gives lane l column l%32 (a row) and the 16 rows
@@ -554,7 +573,8 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pm
 // row's 64 keys are thus split over lanes l and l^32; its max is one
 // cross-lane exchange and its sum is deferred to the end.  The register
 // layout of S^T is directly the P^T operand of the next product (same key
-// order on the V side), so no shuffle sits between the two products.
+// order on the V side), so no shuffle sits between the two products.  bf16
+// runs a tile as two staggered 32-key halves (see compute_tile_bf16).
 
 // LDS tiles.  bf16: K and V both row-major with unpadded 128-byte rows,
 // XOR-swizzled at 16-byte-chunk granularity (K chunk c of row r at slot
@@ -624,8 +644,12 @@ prefill_kernel(const PrefillArgs a) {
   const float qk_scale_log2 = a.qk_scale_log2;
   constexpr int ES = Cfg::ES, KROW = Cfg::KROW, VROW = Cfg::VROW, NT = Cfg::NT;
   constexpr int BK = 64;  // keys per tile
-  __shared__ __attribute__((aligned(16))) char lds_k[2][BK * KROW * ES];
-  __shared__ __attribute__((aligned(16))) char lds_v[2][kHeadDim * VROW * ES];
+  // bf16 ragged: three-stage ring filled by direct-to-LDS loads; otherwise
+  // two stages filled through registers
+  constexpr bool kDma = DT == DT_BF16 && !PAGED;
+  constexpr int NSTAGE = kDma ? 3 : 2;
+  __shared__ __attribute__((aligned(16))) char lds_k[NSTAGE][BK * KROW * ES];
+  __shared__ __attribute__((aligned(16))) char lds_v[NSTAGE][kHeadDim * VROW * ES];
 
   // 1-D grid, (sequence, kv head) pair fastest and query tiles from the last
   // (longest causal key range) to the first: the dispatcher hands out the
@@ -686,6 +710,37 @@ prefill_kernel(const PrefillArgs a) {
     head[rb] = kvh * group + hl;
     valid[rb] = (tl < TW) && (tok[rb] < Lq);
     lim[rb] = valid[rb] ? min(causal ? min(tok[rb] + shift, Lkv - 1) : Lkv - 1, c_hi - 1) : -1;
+  }
+
+  // ---- direct-to-LDS staging (kDma): tile jt goes to stage jt % 3.  Wave w
+  // fills key rows 8(w + 4u) .. +7 of the K and V tiles (u = 0, 1), 1 KB per
+  // load; lane i brings the 16-byte chunk that belongs in slot i % 8 of its
+  // row, so the tiles land in the swizzled layouts the operand reads expect
+  // (K chunk c at slot c ^ (r & 7), V chunk c at slot c ^ 2(r & 3)).  Keys
+  // past the sequence read zero.  The first two tiles are issued before Q.
+  u32x4 kw = {0, 0, 0, 0}, vw = {0, 0, 0, 0};
+  auto dma_issue = [&](int jt) __attribute__((always_inline)) {
+    if constexpr (kDma) {
+      const uint32_t row_bytes = (uint32_t)hkv * kHeadDim * ES;
+      const int key0 = c_lo + jt * BK, stage = jt % NSTAGE;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int key = 8 * (w + 4 * u) + (lane >> 3), slot = lane & 7;
+        const uint32_t row = (uint32_t)(key0 + key) * row_bytes + (uint32_t)kvh * kHeadDim * ES;
+        const uint32_t dst = 1024 * (w + 4 * u);
+        load_to_lds16(kw, row + 16 * (slot ^ (key & 7)),
+                      __builtin_amdgcn_readfirstlane(lds_addr(lds_k[stage]) + dst));
+        load_to_lds16(vw, row + 16 * (slot ^ (2 * (key & 3))),
+                      __builtin_amdgcn_readfirstlane(lds_addr(lds_v[stage]) + dst));
+      }
+    }
+  };
+  if constexpr (kDma) {
+    const uint32_t row_bytes = (uint32_t)hkv * kHeadDim * ES;
+    kw = rsrc_words(k + (size_t)k0 * row_bytes, (uint32_t)((size_t)Lkv * row_bytes));
+    vw = rsrc_words(v + (size_t)k0 * row_bytes, (uint32_t)((size_t)Lkv * row_bytes));
+    if (n_tiles > 0) dma_issue(0);
+    if (n_tiles > 1) dma_issue(1);
   }
 
   // ---- Q^T operand: lane group g owns dims [32g, 32g+32)
@@ -872,7 +927,9 @@ prefill_kernel(const PrefillArgs a) {
     }
   };
 
-  auto compute_tile = [&](auto masked, int buf, int jt) {
+  // fp32 (the instance behind the 1e-5 parity tests): the whole 64-key tile
+  // in one pass on v_mfma_f32_32x32x2f32, P kept in fp32.
+  auto compute_tile_f32 = [&](auto masked, int buf, int jt) {
     const char* kd = lds_k[buf];
     const char* vd = lds_v[buf];
     f32x16 sacc[2][RB];
@@ -883,55 +940,19 @@ prefill_kernel(const PrefillArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) sacc[kb][rb][i] = 0.f;
 
-    // S^T = K Q^T.  bf16: k-step outermost so that the 2*RB accumulators
-    // are interleaved and consecutive MFMAs never depend on each other.
-    if constexpr (DT == DT_BF16) {
-      // the K operands of k-step s + 1 are read before the MFMAs of step s
-      auto k_operand = [&](int s, int kb) {
-        const int krw = kb * 32 + col;
-        return *reinterpret_cast<const u32x4*>(kd + krw * 128 + 16 * ((4 * g + s) ^ (krw & 7)));
-      };
-      u32x4 kf[2][2];
-      kf[0][0] = k_operand(0, 0);
-      kf[0][1] = k_operand(0, 1);
+    // S^T = K Q^T
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const char* krow = kd + ((kb * 32 + col) * KROW + 32 * g) * ES;
 #pragma unroll
       for (int s = 0; s < QV; ++s) {
-        if (s + 1 < QV) {
-          kf[(s + 1) & 1][0] = k_operand(s + 1, 0);
-          kf[(s + 1) & 1][1] = k_operand(s + 1, 1);
-        }
+        const u32x4 kf = *reinterpret_cast<const u32x4*>(krow + 16 * s);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int e = 0; e < 4; ++e)
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb)
-            sacc[kb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8, kf[s & 1][kb]), __builtin_bit_cast(bf16x8, qf[rb][s]),
-                sacc[kb][rb], 0, 0, 0);
-      }
-#if ATTN_SINK_PIPE_ORDER
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-#endif
-    } else {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const char* krow = kd + ((kb * 32 + col) * KROW + 32 * g) * ES;
-#pragma unroll
-        for (int s = 0; s < QV; ++s) {
-          const u32x4 kf = *reinterpret_cast<const u32x4*>(krow + 16 * s);
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb)
-              sacc[kb][rb] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                  __uint_as_float(kf[e]), __uint_as_float(qf[rb][s][e]), sacc[kb][rb], 0, 0, 0);
-        }
+            sacc[kb][rb] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                __uint_as_float(kf[e]), __uint_as_float(qf[rb][s][e]), sacc[kb][rb], 0, 0, 0);
       }
     }
 
@@ -944,8 +965,7 @@ prefill_kernel(const PrefillArgs a) {
     // the tile's row sum exceeds kLaneSumMax (which also catches an
     // infinite P).  The branch is wave-uniform, but only the rows that need
     // it change, so a row's result never depends on other rows.
-    u32x4 pf[RB][2][2];   // bf16 P^T operands [rb][kb][half]
-    float pt[RB][2][16];  // fp32 P^T
+    float pt[RB][2][16];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       if constexpr (decltype(masked)::value) {
@@ -963,32 +983,14 @@ prefill_kernel(const PrefillArgs a) {
       auto form_p = [&](float m) {
         const float m_use = (m == kNegInf) ? 0.f : m;
         float ps[4] = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (DT == DT_BF16) {
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const int r = 8 * hh + 2 * e;
-                const float p0 = fast_exp2(__builtin_fmaf(sacc[kb][rb][r], qk_scale_log2, -m_use));
-                const float p1 =
-                    fast_exp2(__builtin_fmaf(sacc[kb][rb][r + 1], qk_scale_log2, -m_use));
-                pf[rb][kb][hh][e] = pack_bf16x2(p0, p1);
-                // the row sum adds the fp32 P: v_dot2 on the packed pair would
-                // issue to the matrix pipe and stall beside the MFMAs
-                ps[e] += p0 + p1;
-              }
-        } else {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const float pr = fast_exp2(__builtin_fmaf(sacc[kb][rb][r], qk_scale_log2, -m_use));
-              pt[rb][kb][r] = pr;
-              ps[r & 3] += pr;
-            }
-        }
+          for (int r = 0; r < 16; ++r) {
+            const float pr = fast_exp2(__builtin_fmaf(sacc[kb][rb][r], qk_scale_log2, -m_use));
+            pt[rb][kb][r] = pr;
+            ps[r & 3] += pr;
+          }
         return (ps[0] + ps[1]) + (ps[2] + ps[3]);
       };
       float rs = form_p(m_run[rb]);
@@ -1019,87 +1021,294 @@ prefill_kernel(const PrefillArgs a) {
       d_run[rb] += rs;
     }
 
-    // O^T += V^T P^T.  bf16: key step outermost, both dim blocks' V^T
-    // operands read together, so the 2*RB accumulators interleave.
-    if constexpr (DT == DT_BF16) {
-      // source lane s of each 16-lane group points at V[kbase + s/4][dim0 +
-      // 4*(s%4)]; after the transposing read lane i holds V[kbase + 0..3]
-      // [dim0 + i] with dim0 + i = 32*db + lane%32
-      // (paged: the V^T tile is dim-major already; lane (g, col) reads pair
-      // 2(2kb + hh) + g of dim row 32db + col)
-      typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-      const int sl = lane & 15;
-      // V^T operand of dim block db for key step (kb, hh)
-      auto v_operand = [&](int kb, int hh, int db) {
-        if constexpr (PAGED) {
-          const int dim = 32 * db + col, pr = 2 * (2 * kb + hh) + g;
-          return *reinterpret_cast<const u32x4*>(vd + dim * 128 + 16 * (pr ^ ((dim >> 1) & 7)));
-        } else {
-          const int r0 = kb * 32 + 16 * hh + 4 * g + (sl >> 2), r1 = r0 + 8;
-          const int dim = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (sl & 3);
-          const int chunk = dim >> 3, sub = 2 * (dim & 7);
-          const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_i16x4*)(vd + r0 * 128 + 16 * (chunk ^ (2 * (r0 & 3))) + sub));
-          const i16x4 c = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_i16x4*)(vd + r1 * 128 + 16 * (chunk ^ (2 * (r1 & 3))) + sub));
-          const u32x2 lo = __builtin_bit_cast(u32x2, a), hi = __builtin_bit_cast(u32x2, c);
-          return u32x4{lo[0], lo[1], hi[0], hi[1]};
-        }
-      };
-      // the operands of key step t + 1 are read before the MFMAs of step t
-      u32x4 vf[2][2];
-      vf[0][0] = v_operand(0, 0, 0);
-      vf[0][1] = v_operand(0, 0, 1);
+    // O^T += V^T P^T
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        if (t + 1 < 4) {
-          vf[(t + 1) & 1][0] = v_operand((t + 1) >> 1, (t + 1) & 1, 0);
-          vf[(t + 1) & 1][1] = v_operand((t + 1) >> 1, (t + 1) & 1, 1);
+    for (int db = 0; db < 2; ++db) {
+      const char* vrow = vd + ((db * 32 + col) * VROW) * ES;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          const u32x4 vf = *reinterpret_cast<const u32x4*>(vrow + (kb * 32 + 8 * qd + 4 * g) * ES);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+              acc_o[db][rb] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                  __uint_as_float(vf[e]), pt[rb][kb][4 * qd + e], acc_o[db][rb], 0, 0, 0);
         }
+    }
+  };
+
+  // Per-lane byte offsets of the bf16 MFMA operands inside a stage.  Key
+  // blocks, key steps and dim blocks then differ by constants that the LDS
+  // reads take as immediate offsets, so a tile adds its stage base once per
+  // offset.  The XOR swizzles only see bits that those constants leave alone.
+  //  K, k-step s (key block kb: +4096): row col, chunk (4g + s) ^ (col & 7).
+  //  V ragged, dim block db (key rows +32kb +16hh, second half +8 rows):
+  //    rows 4g + sl/4, chunk ((32db + 16((lane>>4)&1) + 4(sl&3)) >> 3) ^
+  //    2((sl/4)&3), byte 8(sl&1) of it, sl = lane % 16 (the transposing read
+  //    hands lane i element i of four 4-element rows).
+  //  V paged, key step t = 2kb + hh (dim block db: +4096): dim row col, pair
+  //    (2t + g) ^ ((col >> 1) & 7).
+  int k_off[4], v_off[PAGED ? 4 : 2];
+#pragma unroll
+  for (int s4 = 0; s4 < 4; ++s4) k_off[s4] = col * 128 + 16 * ((4 * g + s4) ^ (col & 7));
+  if constexpr (PAGED) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) v_off[t] = col * 128 + 16 * ((2 * t + g) ^ ((col >> 1) & 7));
+  } else {
+    const int sl = lane & 15;
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+      const int chunk = (32 * db + 16 * ((lane >> 4) & 1) + 4 * (sl & 3)) >> 3;
+      v_off[db] = (4 * g + (sl >> 2)) * 128 + 16 * (chunk ^ (2 * ((sl >> 2) & 3))) + 8 * (sl & 1);
+    }
+  }
+
+  // bf16: the tile runs as two halves of 32 keys (kb = 0, 1) whose products
+  // and softmax are staggered -- S^T of half 1 beside the softmax of half 0,
+  // O^T += V^T P^T of half 0 beside the softmax of half 1 -- so that every
+  // wave has MFMA and VALU work in the same instruction window.  The halves
+  // read disjoint K and V operands, so no operand stays live across them.
+  // Each half takes the reference check of the full-tile body on its own.
+  auto compute_tile_bf16 = [&](auto masked, int buf, int jt) __attribute__((always_inline)) {
+    const char* kd = lds_k[buf];
+    const char* vd = lds_v[buf];
+    f32x16 sacc[2][RB];
+    u32x4 pf[RB][2][2];  // P^T operands [rb][kb][hh]
+    // This stage's operand addresses: stage base + lane offset, one add each
+    // per tile; the empty asm keeps the sums opaque so that the constants
+    // below stay immediate offsets of the LDS reads.
+    typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const uint32_t kbase = __builtin_amdgcn_readfirstlane(lds_addr(kd));
+    const uint32_t vbase = __builtin_amdgcn_readfirstlane(lds_addr(vd));
+    uint32_t ka[4], va[PAGED ? 4 : 2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ka[i] = kbase + (uint32_t)k_off[i];
+      asm volatile("" : "+v"(ka[i]));
+    }
+#pragma unroll
+    for (int i = 0; i < (PAGED ? 4 : 2); ++i) {
+      va[i] = vbase + (uint32_t)v_off[i];
+      asm volatile("" : "+v"(va[i]));
+    }
+    // K operand of k-step s, key block kb: key row 32kb + col, chunk 4g + s
+    auto k_operand = [&](int s, int kb) __attribute__((always_inline)) {
+      return *(lds_u32x4*)(size_t)(ka[s] + kb * 4096);
+    };
+    // V^T operand of dim block db for key step (kb, hh)
+    auto v_operand = [&](int kb, int hh, int db) __attribute__((always_inline)) {
+      if constexpr (PAGED) {
+        return *(lds_u32x4*)(size_t)(va[2 * kb + hh] + db * 4096);
+      } else {
+        // key rows r0 = 32kb + 16hh + 4g + sl/4 and r0 + 8
+        const uint32_t p = va[db] + (32 * kb + 16 * hh) * 128;
+        const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(size_t)p);
+        const i16x4 c =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(size_t)(p + 8 * 128));
+        const u32x2 lo = __builtin_bit_cast(u32x2, a), hi = __builtin_bit_cast(u32x2, c);
+        return u32x4{lo[0], lo[1], hi[0], hi[1]};
+      }
+    };
+    // S^T of half kb: 4 k-steps x RB MFMAs, K operands of step s + 1 read
+    // before the MFMAs of step s
+    auto qk = [&](int kb) __attribute__((always_inline)) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[kb][rb][i] = 0.f;
+      u32x4 kf[2];
+      kf[0] = k_operand(0, kb);
+#pragma unroll
+      for (int s = 0; s < QV; ++s) {
+        if (s + 1 < QV) kf[(s + 1) & 1] = k_operand(s + 1, kb);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          sacc[kb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, kf[s & 1]), __builtin_bit_cast(bf16x8, qf[rb][s]),
+              sacc[kb][rb], 0, 0, 0);
+      }
+    };
+    // O^T += V^T P^T over the 32 keys of half kb (key steps hh = 0, 1)
+    auto pv = [&](int kb) __attribute__((always_inline)) {
+      u32x4 vf[2][2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int db = 0; db < 2; ++db) vf[hh][db] = v_operand(kb, hh, db);
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
         for (int db = 0; db < 2; ++db)
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb)
             acc_o[db][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8, vf[t & 1][db]),
-                __builtin_bit_cast(bf16x8, pf[rb][t >> 1][t & 1]), acc_o[db][rb], 0, 0, 0);
+                __builtin_bit_cast(bf16x8, vf[hh][db]),
+                __builtin_bit_cast(bf16x8, pf[rb][kb][hh]), acc_o[db][rb], 0, 0, 0);
+    };
+    auto mask = [&](int kb) __attribute__((always_inline)) {
+      if constexpr (decltype(masked)::value) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const int thr = lim[rb] - (c_lo + jt * BK + kb * 32 + 4 * g);
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            sacc[kb][rb][r] = (8 * (r >> 2) + (r & 3) > thr) ? kNegInf : sacc[kb][rb][r];
+        }
       }
-#if ATTN_SINK_PIPE_ORDER
-      __builtin_amdgcn_sched_group_barrier(0x100, PAGED ? 2 : 4, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, PAGED ? 2 : 4, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, PAGED ? 2 : 4, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, PAGED ? 2 : 4, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-#endif
-    } else {
+    };
+    // P of (half kb, row block rb) against reference m; returns the lane's
+    // share of the row sum (the reference-check path)
+    auto form_p = [&](int kb, int rb, float m) __attribute__((always_inline)) {
+      const float m_use = (m == kNegInf) ? 0.f : m;
+      float ps[4];
 #pragma unroll
-      for (int db = 0; db < 2; ++db) {
-        const char* vrow = vd + ((db * 32 + col) * VROW) * ES;
+      for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int e = 0; e < 4; ++e) {
+          const int r = 8 * hh + 2 * e;
+          const float p0 = fast_exp2(__builtin_fmaf(sacc[kb][rb][r], qk_scale_log2, -m_use));
+          const float p1 = fast_exp2(__builtin_fmaf(sacc[kb][rb][r + 1], qk_scale_log2, -m_use));
+          pf[rb][kb][hh][e] = pack_bf16x2(p0, p1);
+          ps[e] = hh == 0 ? p0 + p1 : ps[e] + (p0 + p1);
+        }
+      return (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    };
+    // Common path, one logit pair at a time: pair q = 0..15 of half kb is
+    // row block q / 8, key step (q / 4) % 2, register pair q % 4.
+    float mneg[RB], ps[RB][4], rs[RB];
+    bool slow[RB];
+    auto pair_p = [&](int kb, int q) __attribute__((always_inline)) {
+      const int rb = q >> 3, hh = (q >> 2) & 1, e = q & 3, r = 8 * hh + 2 * e;
+      const float p0 = fast_exp2(__builtin_fmaf(sacc[kb][rb][r], qk_scale_log2, mneg[rb]));
+      const float p1 = fast_exp2(__builtin_fmaf(sacc[kb][rb][r + 1], qk_scale_log2, mneg[rb]));
+      pf[rb][kb][hh][e] = pack_bf16x2(p0, p1);
+      ps[rb][e] = hh == 0 ? p0 + p1 : ps[rb][e] + (p0 + p1);
+    };
+    auto start_half = [&]() __attribute__((always_inline)) {
 #pragma unroll
-          for (int qd = 0; qd < 4; ++qd) {
-            const u32x4 vf =
-                *reinterpret_cast<const u32x4*>(vrow + (kb * 32 + 8 * qd + 4 * g) * ES);
+      for (int rb = 0; rb < RB; ++rb) mneg[rb] = m_run[rb] == kNegInf ? 0.f : -m_run[rb];
+    };
+    // row sums, the reference check (one wave-uniform branch per half, so
+    // the common path of both row blocks stays ahead of it) and d
+    auto end_half = [&](int kb) __attribute__((always_inline)) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
+      for (int rb = 0; rb < RB; ++rb) {
+        rs[rb] = (ps[rb][0] + ps[rb][1]) + (ps[rb][2] + ps[rb][3]);
+        slow[rb] = !(rs[rb] <= kLaneSumMax) || m_run[rb] == kNegInf;
+      }
+      if (wave_any(slow[0] || slow[RB - 1])) {
 #pragma unroll
-              for (int rb = 0; rb < RB; ++rb)
-                acc_o[db][rb] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                    __uint_as_float(vf[e]), pt[rb][kb][4 * qd + e], acc_o[db][rb], 0, 0, 0);
-          }
+        for (int rb = 0; rb < RB; ++rb) {
+          if (!wave_any(slow[rb])) continue;
+          const bool need = xor_max(slow[rb] ? 1.f : 0.f, 32) > 0.f;
+          float mx4[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
+#pragma unroll
+          for (int r = 0; r < 16; r += 2)
+            mx4[(r / 2) & 3] = fmaxf(fmaxf(mx4[(r / 2) & 3], sacc[kb][rb][r]), sacc[kb][rb][r + 1]);
+          const float mx =
+              xor_max(fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3])), 32) * qk_scale_log2;
+          const float m_new = need ? fmaxf(m_run[rb], mx) : m_run[rb];
+          const float alpha = (m_new == m_run[rb]) ? 1.f : fast_exp2(m_run[rb] - m_new);
+          d_run[rb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < 2; ++db) acc_o[db][rb] *= alpha;
+          m_run[rb] = m_new;
+          rs[rb] = form_p(kb, rb, m_new);
+        }
+      }
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) d_run[rb] += rs[rb];
+    };
+    static_assert(RB == 2, "the staggered schedule pairs two row blocks");
+    // scheduling fence: instructions are not moved across it
+#define ATTN_SINK_FENCE() __builtin_amdgcn_sched_barrier(0)
+    // S^T of half 0, with the first K operand of half 1 read early
+    qk(0);
+    u32x4 kf[2];
+    kf[0] = k_operand(0, 1);
+    mask(0);
+    start_half();
+    ATTN_SINK_FENCE();
+    // S^T of half 1: each MFMA followed by two logit pairs of half 0
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[1][rb][i] = 0.f;
+#pragma unroll
+    for (int s = 0; s < QV; ++s) {
+      if (s + 1 < QV) kf[(s + 1) & 1] = k_operand(s + 1, 1);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        sacc[1][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8, kf[s & 1]), __builtin_bit_cast(bf16x8, qf[rb][s]),
+            sacc[1][rb], 0, 0, 0);
+        ATTN_SINK_FENCE();
+        pair_p(0, 2 * (2 * s + rb));
+        pair_p(0, 2 * (2 * s + rb) + 1);
+        ATTN_SINK_FENCE();
       }
     }
+    end_half(0);
+    // O^T += V^T P^T of half 0: each MFMA followed by two logit pairs of half 1
+    mask(1);
+    start_half();
+    u32x4 vf[2][2];
+    vf[0][0] = v_operand(0, 0, 0);
+    vf[0][1] = v_operand(0, 0, 1);
+    vf[1][0] = v_operand(0, 1, 0);
+    vf[1][1] = v_operand(0, 1, 1);
+    ATTN_SINK_FENCE();
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          acc_o[db][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, vf[hh][db]), __builtin_bit_cast(bf16x8, pf[rb][0][hh]),
+              acc_o[db][rb], 0, 0, 0);
+          ATTN_SINK_FENCE();
+          const int q = 2 * (4 * hh + 2 * db + rb);
+          pair_p(1, q);
+          pair_p(1, q + 1);
+          ATTN_SINK_FENCE();
+        }
+    end_half(1);
+    pv(1);
+#undef ATTN_SINK_FENCE
   };
 
   // Tiles below n_plain need no mask for any valid row of the workgroup; the
   // remaining (diagonal / ragged-tail) tiles run the masked body.  Two loops
   // keep the mask arithmetic out of the common path.
   const int n_plain = min(n_tiles, max(0, (lim_min + 1 - c_lo) / BK));
-  if (n_tiles > 0) {
+  if constexpr (kDma) {
+    // Q and the first two tiles were issued together: wait for all of them
+    // (a wait the compiler sees, so it adds none for Q later), then per tile
+    // issue tile jt + 2, compute tile jt, wait until only tile jt + 2's four
+    // loads are outstanding (tile jt + 1 has landed), and barrier.  The
+    // barrier also frees stage jt % 3 for tile jt + 3.
+    auto tile_step = [&](auto masked, int jt) __attribute__((always_inline)) {
+      if (jt + 2 < n_tiles) dma_issue(jt + 2);
+      compute_tile_bf16(masked, jt % NSTAGE, jt);
+      if (jt + 2 < n_tiles)
+        asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      lds_barrier();
+    };
+    if (n_tiles > 0) {
+      __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+      lds_barrier();
+      int jt = 0;
+      for (; jt < n_plain; ++jt) tile_step(std::false_type{}, jt);
+      for (; jt < n_tiles; ++jt) tile_step(std::true_type{}, jt);
+    }
+  } else if (n_tiles > 0) {
     fetch_ids(0);
     stage_load(0);
     stage_store(0);
@@ -1108,14 +1317,20 @@ prefill_kernel(const PrefillArgs a) {
     for (; jt < n_plain; ++jt) {
       const bool more = jt + 1 < n_tiles;
       if (more) stage_load(jt + 1);
-      compute_tile(std::false_type{}, jt & 1, jt);
+      if constexpr (DT == DT_BF16)
+        compute_tile_bf16(std::false_type{}, jt & 1, jt);
+      else
+        compute_tile_f32(std::false_type{}, jt & 1, jt);
       if (more) stage_store((jt + 1) & 1);
       __syncthreads();
     }
     for (; jt < n_tiles; ++jt) {
       const bool more = jt + 1 < n_tiles;
       if (more) stage_load(jt + 1);
-      compute_tile(std::true_type{}, jt & 1, jt);
+      if constexpr (DT == DT_BF16)
+        compute_tile_bf16(std::true_type{}, jt & 1, jt);
+      else
+        compute_tile_f32(std::true_type{}, jt & 1, jt);
       if (more) stage_store((jt + 1) & 1);
       __syncthreads();
     }
