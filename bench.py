@@ -7,6 +7,8 @@ One step = one pass over every stage of the path on its synthetic workload:
   paged    the prefill workload with keys and values in a paged cache
   chunked  chunked prefill: B=1, 512 new tokens on a 32768-key paged cache,
            unsplit, then split (default_prefill_splits: 4) + merge
+  ragged   ragged causal prefill, 16 sequences U[128,4096], sinks -inf / 0 /
+           N(0,1) / +20, logits up to about +-30 (reported, not in value)
 `value` is the prefill throughput in TFLOP/s (algorithmic flops: 4*D per
 causal-visible (query, key) pair) from HIP events around the prefill launch
 on the stream it runs on; the decode stages report achieved HBM GB/s.  The
@@ -152,6 +154,17 @@ def main():
     p6 = mk_partials(c6["q"].shape[0], s6)
     o6 = torch.empty_like(c6["q"])
 
+    # The ragged edge-case prefill workload (16 sequences, lengths U[128,4096],
+    # sinks -inf / 0 / N(0,1) / +20, logits up to about +-30): reported beside
+    # the main prefill figure, not part of value.
+    c5 = workloads.workload(5, device=dev)
+    out5 = torch.empty_like(c5["q"])
+    mq5 = max(c5["lens_q"])
+
+    def run_ragged_prefill():
+        attn.attn_sink_prefill(c5["q"], c5["k"], c5["v"], c5["sinks"], c5["cu_seqlens_q"],
+                               c5["cu_seqlens_kv"], mq5, 8, c5["sm_scale"], True, out=out5)
+
     def run_paged_prefill():
         attn.attn_sink_prefill_paged(c2["q"], pk2["k_cache"], pk2["v_cache"], pk2["page_table"],
                                      c2["cu_seqlens_q"], pk2["kv_lens"], c2["sinks"], 2048, 8,
@@ -178,6 +191,7 @@ def main():
         ("chunked", lambda: run_chunked(1)),
         ("chunked_split", lambda: run_chunked(s6)),
         ("chunked_merge", lambda: attn.attn_sink_merge(*p6, out=o6)),
+        ("ragged_prefill", run_ragged_prefill),
     ]
 
     def step(evs=None):
@@ -220,6 +234,9 @@ def main():
     tf2p = fl2p / (t["paged_prefill"] * 1e-3) / 1e12
     tf6 = fl6 / (t["chunked"] * 1e-3) / 1e12
     tf6s = fl6 / ((t["chunked_split"] + t["chunked_merge"]) * 1e-3) / 1e12
+
+    fl5 = prefill_flops(c5["lens_q"], c5["lens_kv"], hq, 64)
+    tf5 = fl5 / (t["ragged_prefill"] * 1e-3) / 1e12
 
     traffic = counted_traffic() or {}
     result = {
@@ -277,6 +294,11 @@ def main():
                             "us_merge": round(t["chunked_merge"] * 1e3, 2),
                             "TFLOP/s_split": round(tf6s, 2),
                             "frac_split": round(tf6s / PEAK_BF16_TFLOPS, 4)},
+        "ragged_prefill": {"workload": c5["name"], "flops": fl5,
+                           "us": round(t["ragged_prefill"] * 1e3, 2),
+                           "TFLOP/s": round(tf5, 2),
+                           "frac": round(tf5 / PEAK_BF16_TFLOPS, 4),
+                           "traffic": traffic.get("ragged_prefill")},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(c2, args.cpu_seconds)

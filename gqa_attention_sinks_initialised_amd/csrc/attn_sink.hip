@@ -128,6 +128,20 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t v
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
+// Index of the sequence with the r-th largest length among n <= 64 (ties by
+// index), one length per lane (lanes >= n hold -1): each lane counts the
+// lengths that beat its own, one compare per lane and step.  r < n.
+__device__ __forceinline__ int nth_longest(int len, int n, int r) {
+  const int lane = threadIdx.x & 63;
+  int rank = 0;
+  for (int j = 0; j < n; ++j) {
+    const int lj = __builtin_amdgcn_readlane(len, j);
+    rank += (lj > len) || (lj == len && j < lane);
+  }
+  const uint64_t hit = __builtin_amdgcn_ballot_w64(lane < n && rank == r);
+  return __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(hit));
+}
+
 // Buffer resource words over [base, base + bytes) (the same descriptor as
 // make_rsrc), for the loads issued from inline assembly below.
 __device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
@@ -210,21 +224,14 @@ __global__ __launch_bounds__(64 * WAVES, (DT == DT_BF16 ? ATTN_SINK_DECODE_MIN_W
   const int lane = threadIdx.x & 63;
   // Longest sequences first: workgroups are dispatched in blockIdx order, so
   // for up to 64 sequences blockIdx.z is read as a rank and mapped to the
-  // sequence with the rank-th largest kv_len (ties by index).  Each wave
-  // ranks the 64 lengths with one compare per lane and step.
-  // The rank search leaves every length in a register, so the sequence's own
-  // length costs no second dependent load.
+  // sequence with the rank-th largest kv_len (ties by index).  The ranking
+  // leaves every length in a register, so the sequence's own length costs no
+  // second dependent load.
   int b = blockIdx.z, L;
   const int batch = gridDim.z;
   if (batch <= 64) {
     const int li = lane < batch ? clampi(kv_lens[lane], 0, max_pages * kPage) : -1;
-    int rank = 0;
-    for (int j = 0; j < batch; ++j) {
-      const int lj = __builtin_amdgcn_readlane(li, j);
-      rank += (lj > li) || (lj == li && j < lane);
-    }
-    const uint64_t hit = __builtin_amdgcn_ballot_w64(lane < batch && rank == (int)blockIdx.z);
-    b = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(hit));
+    b = nth_longest(li, batch, (int)blockIdx.z);
     L = __builtin_amdgcn_readlane(li, b);
   } else {
     L = clampi(kv_lens[b], 0, max_pages * kPage);
@@ -612,6 +619,7 @@ struct PrefillArgs {
   float* pd;
   float* po;
   int total_q, total_kv, hkv, group, causal, n_qtiles, n_pairs, splits, max_pages, num_pages;
+  int rank_seqs;  // map pair ranks to sequences by decreasing query length
   uint32_t cache_bytes;  // bytes of each paged cache
   float qk_scale_log2;
 };
@@ -662,7 +670,7 @@ prefill_kernel(const PrefillArgs a) {
   const int split = SPLIT ? slot % a.splits : 0;
   if constexpr (SPLIT) slot /= a.splits;
   const int tile = n_qtiles - 1 - slot;
-  const int kvh = pair % hkv, b = pair / hkv;
+  const int kvh = pair % hkv;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, col = lane & 31;
@@ -670,13 +678,39 @@ prefill_kernel(const PrefillArgs a) {
   const int TW = Cfg::ROWS / group;  // tokens per wave
   const int TB = WAVES * TW;         // tokens per workgroup
 
-  const int q0 = clampi(a.cu_q[b], 0, total_q), q1 = clampi(a.cu_q[b + 1], q0, total_q);
-  int k0 = 0, Lkv;
-  if constexpr (PAGED) {
-    Lkv = clampi(a.kv_lens[b], 0, a.max_pages * kPage);
+  // For up to 64 sequences of unequal query length the pair's sequence
+  // index is read as a rank by decreasing query length (ties by index):
+  // within a slot, the workgroups with work are then contiguous and those of
+  // sequences too short for the slot's tile (which exit at once) trail them.
+  // Interleaved, those empty workgroups skewed the placement of the rest (16
+  // ragged sequences: 20% slower).  Every lane loads its own sequence's
+  // bounds, so the ranking adds no dependent load.
+  const int batch = n_pairs / hkv;
+  int b = pair / hkv, q0, q1, k0 = 0, Lkv;
+  if (a.rank_seqs) {
+    const int bl = min(lane, batch), bh = min(lane + 1, batch);
+    const int cq0 = clampi(a.cu_q[bl], 0, total_q), cq1 = clampi(a.cu_q[bh], cq0, total_q);
+    int lk0 = 0, lk1;
+    if constexpr (PAGED) {
+      lk1 = clampi(a.kv_lens[min(lane, batch - 1)], 0, a.max_pages * kPage);
+    } else {
+      lk0 = clampi(a.cu_kv[bl], 0, a.total_kv);
+      lk1 = clampi(a.cu_kv[bh], lk0, a.total_kv);
+    }
+    b = nth_longest(lane < batch ? cq1 - cq0 : -1, batch, b);
+    q0 = __builtin_amdgcn_readlane(cq0, b);
+    q1 = __builtin_amdgcn_readlane(cq1, b);
+    k0 = __builtin_amdgcn_readlane(lk0, b);
+    Lkv = __builtin_amdgcn_readlane(lk1, b) - k0;
   } else {
-    k0 = clampi(a.cu_kv[b], 0, a.total_kv);
-    Lkv = clampi(a.cu_kv[b + 1], k0, a.total_kv) - k0;
+    q0 = clampi(a.cu_q[b], 0, total_q);
+    q1 = clampi(a.cu_q[b + 1], q0, total_q);
+    if constexpr (PAGED) {
+      Lkv = clampi(a.kv_lens[b], 0, a.max_pages * kPage);
+    } else {
+      k0 = clampi(a.cu_kv[b], 0, a.total_kv);
+      Lkv = clampi(a.cu_kv[b + 1], k0, a.total_kv) - k0;
+    }
   }
   const int Lq = q1 - q0;
   const int t_begin = tile * TB;
@@ -1412,6 +1446,9 @@ int launch_prefill(PrefillArgs a, int dtype, int batch, int max_seqlen_q, hipStr
   const int waves = dtype == ATTN_SINK_BF16 ? kPrefillWaves : 4;
   const int tb = waves * (64 / a.group);  // waves of 64 rows
   a.n_qtiles = (max_seqlen_q + tb - 1) / tb;
+  // With every query length equal to max_seqlen_q no slot has empty
+  // workgroups, and the ranking would only lengthen the prologue.
+  a.rank_seqs = batch <= 64 && (int64_t)batch * max_seqlen_q != (int64_t)a.total_q;
   const int64_t blocks = (int64_t)a.n_qtiles * a.n_pairs * (SPLIT ? a.splits : 1);
   if (blocks > INT32_MAX) return ATTN_SINK_ERR_UNSUPPORTED;
   const dim3 grid((unsigned)blocks);
