@@ -620,6 +620,7 @@ struct PrefillArgs {
   float* po;
   int total_q, total_kv, hkv, group, causal, n_qtiles, n_pairs, splits, max_pages, num_pages;
   int rank_seqs;  // map pair ranks to sequences by decreasing query length
+  int seq_major;  // with rank_seqs: sequence-major order within each XCD
   uint32_t cache_bytes;  // bytes of each paged cache
   float qk_scale_log2;
 };
@@ -667,10 +668,10 @@ prefill_kernel(const PrefillArgs a) {
   // With SPLIT, the chunks of one query tile are adjacent in dispatch order.
   const int pair = (int)(blockIdx.x % (unsigned)n_pairs);
   int slot = (int)(blockIdx.x / (unsigned)n_pairs);
-  const int split = SPLIT ? slot % a.splits : 0;
+  int split = SPLIT ? slot % a.splits : 0;
   if constexpr (SPLIT) slot /= a.splits;
-  const int tile = n_qtiles - 1 - slot;
-  const int kvh = pair % hkv;
+  int tile = n_qtiles - 1 - slot;
+  int kvh = pair % hkv;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, col = lane & 31;
@@ -685,6 +686,17 @@ prefill_kernel(const PrefillArgs a) {
   // Interleaved, those empty workgroups skewed the placement of the rest (16
   // ragged sequences: 20% slower).  Every lane loads its own sequence's
   // bounds, so the ranking adds no dependent load.
+  //
+  // With seq_major (ragged batch and keys, kv heads a multiple of the 8
+  // XCDs) the order is
+  // instead sequence-major within each XCD: workgroup i runs on XCD i % 8
+  // (workgroups go round-robin over XCDs), which takes kv heads x, x + 8, ...
+  // and walks their work items sequence by sequence, longest first, each
+  // sequence's query tiles heaviest first (chunks of a tile adjacent).  Only
+  // one or two sequences' K/V are then live in an XCD's L2 at a time, where
+  // the slot-major order keeps every sequence's live (16 ragged sequences:
+  // 8.6 MB of K/V per XCD against a 4 MB L2).  Each XCD does the same work;
+  // workgroups past an XCD's last item exit.
   const int batch = n_pairs / hkv;
   int b = pair / hkv, q0, q1, k0 = 0, Lkv;
   if (a.rank_seqs) {
@@ -697,7 +709,30 @@ prefill_kernel(const PrefillArgs a) {
       lk0 = clampi(a.cu_kv[bl], 0, a.total_kv);
       lk1 = clampi(a.cu_kv[bh], lk0, a.total_kv);
     }
-    b = nth_longest(lane < batch ? cq1 - cq0 : -1, batch, b);
+    const int len = lane < batch ? cq1 - cq0 : -1;
+    if (!PAGED && a.seq_major) {
+      const int S = SPLIT ? a.splits : 1, hpx = hkv / 8;
+      const int j = (int)(blockIdx.x / 8u);
+      const int ntq = len > 0 ? (len + TB - 1) / TB : 0;  // query tiles of this lane's sequence
+      const int items = ntq * S * hpx;
+      // items of the sequences ordered before this lane's (longer, or as
+      // long with a lower index)
+      int start = 0;
+      for (int m = 0; m < batch; ++m) {
+        const int lm = __builtin_amdgcn_readlane(len, m), im = __builtin_amdgcn_readlane(items, m);
+        start += ((lm > len) || (lm == len && m < lane)) ? im : 0;
+      }
+      const uint64_t hit = __builtin_amdgcn_ballot_w64(lane < batch && start <= j && j < start + items);
+      if (hit == 0) return;
+      b = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(hit));
+      const int local = j - __builtin_amdgcn_readlane(start, b);
+      const int per_head = __builtin_amdgcn_readlane(ntq, b) * S;
+      kvh = (int)(blockIdx.x % 8u) + 8 * (local / per_head);
+      split = (local % per_head) % S;
+      tile = __builtin_amdgcn_readlane(ntq, b) - 1 - (local % per_head) / S;
+    } else {
+      b = nth_longest(len, batch, b);
+    }
     q0 = __builtin_amdgcn_readlane(cq0, b);
     q1 = __builtin_amdgcn_readlane(cq1, b);
     k0 = __builtin_amdgcn_readlane(lk0, b);
@@ -1449,6 +1484,9 @@ int launch_prefill(PrefillArgs a, int dtype, int batch, int max_seqlen_q, hipStr
   // With every query length equal to max_seqlen_q no slot has empty
   // workgroups, and the ranking would only lengthen the prologue.
   a.rank_seqs = batch <= 64 && (int64_t)batch * max_seqlen_q != (int64_t)a.total_q;
+  // (ragged keys only: the paged kernels sit at the register limit, and the
+  // extra prologue code cost them 1%)
+  a.seq_major = !PAGED && a.rank_seqs && a.hkv % 8 == 0;
   const int64_t blocks = (int64_t)a.n_qtiles * a.n_pairs * (SPLIT ? a.splits : 1);
   if (blocks > INT32_MAX) return ATTN_SINK_ERR_UNSUPPORTED;
   const dim3 grid((unsigned)blocks);
