@@ -48,6 +48,10 @@ CASES = [
     ([97], None, 6, 2, True),                     # group 3 (does not divide 64)
     ([200], None, 24, 2, False),                  # group 12
     ([129], None, 2, 2, True),                    # group 1 (plain multi-head)
+    # kv heads a multiple of 8 with unequal lengths: the sequence-major order
+    ([130, 7, 0, 257, 64], [200, 7, 5, 257, 64], 16, 8, True),
+    ([100, 33, 300], None, 32, 16, True),         # two kv heads per XCD
+    ([70, 129, 1], [150, 3, 40], 16, 8, False),
 ]
 
 

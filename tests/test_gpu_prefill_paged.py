@@ -159,6 +159,25 @@ def test_ragged_split_partials_and_merge(lib, dtype, splits, causal):
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("splits", [2, 5])
+def test_ragged_split_sequence_major_order(lib, dtype, splits):
+    """Split prefill whose work order is sequence-major per XCD (kv heads a
+    multiple of 8, unequal lengths): every (sequence, head, tile, chunk) is
+    written exactly once."""
+    d = paged_case([3, 130, 1, 0, 64, 257], [85, 130, 600, 5, 64, 257], 16, 8, dtype,
+                   seed=20 + splits)
+    got = run_ragged_partials(lib, d, True, splits)
+    ref = oracle.prefill_partials(d["q"], d["k"], d["v"], d["sinks"], d["cu_seqlens_q"],
+                                  d["cu_seqlens_kv"], 8, 2, d["sm_scale"], True, splits)
+    check_partials(got, ref, dtype, d["sinks"], "ragged seq-major S=%d" % splits)
+    merged = lib.attn_sink_merge(*(t.to(DEV) for t in got), out_dtype=dtype)
+    torch.cuda.synchronize()
+    full = oracle.prefill(d["q"], d["k"], d["v"], d["sinks"], d["cu_seqlens_q"],
+                          d["cu_seqlens_kv"], 8, 2, d["sm_scale"], True)
+    assert_close(merged.cpu(), full, dtype, "ragged seq-major merged")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("splits", [2, 7, 64])
 def test_paged_split_partials_and_merge(lib, dtype, splits):
     d = paged_case([3, 130, 1, 0, 64], [85, 130, 600, 5, 64], 8, 2, dtype, seed=10 + splits)
