@@ -688,15 +688,14 @@ prefill_kernel(const PrefillArgs a) {
   // bounds, so the ranking adds no dependent load.
   //
   // With seq_major (ragged batch and keys, kv heads a multiple of the 8
-  // XCDs) the order is
-  // instead sequence-major within each XCD: workgroup i runs on XCD i % 8
-  // (workgroups go round-robin over XCDs), which takes kv heads x, x + 8, ...
-  // and walks their work items sequence by sequence, longest first, each
-  // sequence's query tiles heaviest first (chunks of a tile adjacent).  Only
-  // one or two sequences' K/V are then live in an XCD's L2 at a time, where
-  // the slot-major order keeps every sequence's live (16 ragged sequences:
-  // 8.6 MB of K/V per XCD against a 4 MB L2).  Each XCD does the same work;
-  // workgroups past an XCD's last item exit.
+  // XCDs) the order is instead sequence-major within each XCD: workgroup i
+  // runs on XCD i % 8 (workgroups go round-robin over XCDs), which takes kv
+  // heads x, x + 8, ... and walks their work items sequence by sequence,
+  // longest first, each sequence's query tiles heaviest first (chunks of a
+  // tile adjacent).  Only one or two sequences' K/V are then live in an
+  // XCD's L2 at a time, where the slot-major order keeps every sequence's
+  // live (16 ragged sequences: 8.6 MB of K/V per XCD against a 4 MB L2).
+  // Each XCD does the same work; workgroups past an XCD's last item exit.
   const int batch = n_pairs / hkv;
   int b = pair / hkv, q0, q1, k0 = 0, Lkv;
   if (a.rank_seqs) {
@@ -846,7 +845,8 @@ prefill_kernel(const PrefillArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc_o[db][rb][i] = 0.f;
 
-  // ---- K/V staging: global (buffer loads, zero past the sequence) -> regs -> LDS
+  // ---- K/V staging of paged and fp32 tiles: global (buffer loads, zero past
+  // the sequence) -> registers -> LDS, one tile ahead
   const uint32_t kv_row_bytes = (uint32_t)hkv * kHeadDim * ES;
   const __amdgpu_buffer_rsrc_t kr =
       PAGED ? make_rsrc(k, a.cache_bytes)
@@ -980,19 +980,15 @@ prefill_kernel(const PrefillArgs a) {
       }
       return;
     }
+    // fp32 ragged V, transposed to dim-major (bf16 ragged tiles are loaded
+    // straight into LDS and never come here)
 #pragma unroll
     for (int u = 0; u < NCV; ++u) {
-      const int c = tid + NT * u, part = c % CPR;
+      const int c = tid + NT * u, part = c % CPR, key = c / CPR;
       if (c >= VITEMS) continue;
-      if constexpr (DT == DT_BF16) {
-        const int key = c / CPR;
-        *reinterpret_cast<u32x4*>(vd + key * 128 + 16 * (part ^ (2 * (key & 3)))) = stv[u][0];
-      } else {
-        const int key = c / CPR;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          *reinterpret_cast<unsigned int*>(vd + ((4 * part + i) * VROW + key) * ES) = stv[u][0][i];
-      }
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<unsigned int*>(vd + ((4 * part + i) * VROW + key) * ES) = stv[u][0][i];
     }
   };
 
