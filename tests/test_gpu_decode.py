@@ -59,6 +59,19 @@ def test_decode_sweep_matches_oracle(lib, dtype, group, splits):
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("splits", [1, 3])
+def test_decode_more_than_64_sequences(lib, dtype, splits):
+    """Past 64 sequences the grid's sequence index is used as is (no ranking
+    by length)."""
+    g = torch.Generator().manual_seed(70 + splits)
+    lens = torch.randint(0, 300, (70,), generator=g).tolist()
+    d = workloads.decode_inputs(lens, hq=8, hkv=2, dtype=dtype, seed=71 + splits, sink_std=1.5)
+    out, _ = run_decode(lib, _to_dev(d), splits)
+    torch.cuda.synchronize()
+    assert_close(out, oracle_decode(d), dtype, "decode B=70 S=%d" % splits)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_partials_match_oracle_and_bookkeeping(lib, dtype):
     """Chunk states: the empty/non-empty pattern and chunk 0's sink-only state
     are exact; finite m, d and o/d match the oracle's partials."""

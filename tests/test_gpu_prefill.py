@@ -66,6 +66,15 @@ def test_prefill_sweep_matches_oracle(lib, dtype, case):
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_prefill_more_than_64_sequences(lib, dtype):
+    """Past 64 sequences the pair index is used as is (no ranking by length)."""
+    g = torch.Generator().manual_seed(65)
+    lens = torch.randint(0, 40, (70,), generator=g).tolist()
+    d = workloads.prefill_inputs(lens, hq=16, hkv=8, dtype=dtype, seed=66, sink_std=1.5)
+    assert_close(run_prefill(lib, d), oracle_prefill(d), dtype, "prefill B=70")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_prefill_sink_extremes(lib, dtype):
     """Sinks -inf, 0, moderate and +20 with logits up to about +-30."""
     sinks = torch.tensor([-math.inf, 0.0, 1.3, 20.0, -math.inf, -2.0, 20.0, 0.5])
