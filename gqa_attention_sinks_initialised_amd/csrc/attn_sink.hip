@@ -656,6 +656,7 @@ prefill_kernel(const PrefillArgs a) {
   // bf16 ragged: three-stage ring filled by direct-to-LDS loads; otherwise
   // two stages filled through registers
   constexpr bool kDma = DT == DT_BF16 && !PAGED;
+  static_assert(!kDma || WAVES == 4 || WAVES == 8, "direct-to-LDS staging splits a tile over 4 or 8 waves");
   constexpr int NSTAGE = kDma ? 3 : 2;
   __shared__ __attribute__((aligned(16))) char lds_k[NSTAGE][BK * KROW * ES];
   __shared__ __attribute__((aligned(16))) char lds_v[NSTAGE][kHeadDim * VROW * ES];
@@ -781,8 +782,8 @@ prefill_kernel(const PrefillArgs a) {
   }
 
   // ---- direct-to-LDS staging (kDma): tile jt goes to stage jt % 3.  Wave w
-  // fills key rows 8(w + 4u) .. +7 of the K and V tiles (u = 0, 1), 1 KB per
-  // load; lane i brings the 16-byte chunk that belongs in slot i % 8 of its
+  // fills key rows 8(w + WAVES u) .. +7 of the K and V tiles (u < 8 / WAVES),
+  // 1 KB per load; lane i brings the 16-byte chunk that belongs in slot i % 8 of its
   // row, so the tiles land in the swizzled layouts the operand reads expect
   // (K chunk c at slot c ^ (r & 7), V chunk c at slot c ^ 2(r & 3)).  Keys
   // past the sequence read zero.  The first two tiles are issued before Q.
@@ -792,10 +793,10 @@ prefill_kernel(const PrefillArgs a) {
       const uint32_t row_bytes = (uint32_t)hkv * kHeadDim * ES;
       const int key0 = c_lo + jt * BK, stage = jt % NSTAGE;
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int key = 8 * (w + 4 * u) + (lane >> 3), slot = lane & 7;
+      for (int u = 0; u < 8 / WAVES; ++u) {
+        const int key = 8 * (w + WAVES * u) + (lane >> 3), slot = lane & 7;
         const uint32_t row = (uint32_t)(key0 + key) * row_bytes + (uint32_t)kvh * kHeadDim * ES;
-        const uint32_t dst = 1024 * (w + 4 * u);
+        const uint32_t dst = 1024 * (w + WAVES * u);
         load_to_lds16(kw, row + 16 * (slot ^ (key & 7)),
                       __builtin_amdgcn_readfirstlane(lds_addr(lds_k[stage]) + dst));
         load_to_lds16(vw, row + 16 * (slot ^ (2 * (key & 3))),
@@ -1360,10 +1361,15 @@ prefill_kernel(const PrefillArgs a) {
     auto tile_step = [&](auto masked, int jt) __attribute__((always_inline)) {
       if (jt + 2 < n_tiles) dma_issue(jt + 2);
       compute_tile_bf16(masked, jt % NSTAGE, jt);
-      if (jt + 2 < n_tiles)
-        asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-      else
+      // tile jt + 2's loads (2 * 8 / WAVES per wave) may stay in flight
+      if (jt + 2 < n_tiles) {
+        if constexpr (WAVES == 4)
+          asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+      } else {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
       lds_barrier();
     };
     if (n_tiles > 0) {
