@@ -179,53 +179,68 @@ def main():
 
     # One step, in launch order.  The kernel sequence of a step (ours only) is
     # fixed, which is how profile summaries attribute dispatches to workloads.
+    # A merge is timed in one bracket with the decode it finishes (third field
+    # True): an event recorded between two launches on a stream leaves a gap
+    # of a few microseconds that is not part of the work.
     ops = [
-        ("prefill", run_prefill),
-        ("_flush", flush.sum),
-        ("decode", lambda: run_decode(c3, s3, p3)),
-        ("decode_merge", lambda: attn.attn_sink_merge(*p3, out=o3)),
-        ("_flush", flush.sum),
-        ("split", lambda: run_decode(c4, s4, p4)),
-        ("split_merge", lambda: attn.attn_sink_merge(*p4, out=o4)),
-        ("paged_prefill", run_paged_prefill),
-        ("chunked", lambda: run_chunked(1)),
-        ("chunked_split", lambda: run_chunked(s6)),
-        ("chunked_merge", lambda: attn.attn_sink_merge(*p6, out=o6)),
-        ("ragged_prefill", run_ragged_prefill),
+        ("prefill", run_prefill, False),
+        ("_flush", flush.sum, False),
+        ("decode", lambda: run_decode(c3, s3, p3), False),
+        ("decode_merge", lambda: attn.attn_sink_merge(*p3, out=o3), True),
+        ("_flush", flush.sum, False),
+        ("split", lambda: run_decode(c4, s4, p4), False),
+        ("split_merge", lambda: attn.attn_sink_merge(*p4, out=o4), True),
+        ("paged_prefill", run_paged_prefill, False),
+        ("chunked", lambda: run_chunked(1), False),
+        ("chunked_split", lambda: run_chunked(s6), False),
+        ("chunked_merge", lambda: attn.attn_sink_merge(*p6, out=o6), True),
+        ("ragged_prefill", run_ragged_prefill, False),
     ]
 
-    def step(evs=None):
-        for i, (_, fn) in enumerate(ops):
-            if evs:
+    def step(evs=None, split_pairs=False):
+        """One step; with events, evs[i] is recorded before op i unless that op
+        continues the previous bracket (and split_pairs is off)."""
+        for i, (_, fn, joined) in enumerate(ops):
+            if evs and (split_pairs or not joined):
                 evs[i].record()
             fn()
         if evs:
             evs[len(ops)].record()
 
+    def timed(n, split_pairs):
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(ops) + 1)]
+               for _ in range(n)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(n):
+            step(evs[i], split_pairs)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        # bracket time (ms) of every op that opens a bracket
+        marks = [i for i, op in enumerate(ops) if split_pairs or not op[2]] + [len(ops)]
+        t = {}
+        for a, b in zip(marks, marks[1:]):
+            if not ops[a][0].startswith("_"):
+                t[ops[a][0]] = sum(e[a].elapsed_time(e[b]) for e in evs) / n
+        return t, wall
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(ops) + 1)]
-           for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
-
-    t = {}
-    for i, (name, _) in enumerate(ops):
-        if not name.startswith("_"):
-            t[name] = sum(e[i].elapsed_time(e[i + 1]) for e in evs) / len(evs)
+    # The K timed steps; then a few more with an event between every launch,
+    # for the per-kernel split of each decode + merge bracket.
+    tb, wall = timed(args.steps, False)
+    t, _ = timed(min(args.steps, 10), True)
+    for name in ("prefill", "paged_prefill", "chunked", "ragged_prefill"):
+        t[name] = tb[name]
 
     fl2 = prefill_flops(c2["lens_q"], c2["lens_kv"], hq, 64)
     tflops = fl2 / (t["prefill"] * 1e-3) / 1e12
     b3 = decode_bytes(c3["kv_lens"].tolist(), hq, 8, 64, s3)
     b4 = decode_bytes(c4["kv_lens"].tolist(), hq, 8, 64, s4)
-    gbs3 = b3["total"] / ((t["decode"] + t["decode_merge"]) * 1e-3) / 1e9
-    gbs4 = b4["total"] / ((t["split"] + t["split_merge"]) * 1e-3) / 1e9
+    gbs3 = b3["total"] / (tb["decode"] * 1e-3) / 1e9
+    gbs4 = b4["total"] / (tb["split"] * 1e-3) / 1e9
     gbs3_k = b3["decode"] / (t["decode"] * 1e-3) / 1e9
     gbs4_k = b4["decode"] / (t["split"] * 1e-3) / 1e9
 
@@ -233,7 +248,7 @@ def main():
     fl6 = prefill_flops(c6["lens_q"], c6["lens_kv"], hq, 64)
     tf2p = fl2p / (t["paged_prefill"] * 1e-3) / 1e12
     tf6 = fl6 / (t["chunked"] * 1e-3) / 1e12
-    tf6s = fl6 / ((t["chunked_split"] + t["chunked_merge"]) * 1e-3) / 1e12
+    tf6s = fl6 / (tb["chunked_split"] * 1e-3) / 1e12
 
     fl5 = prefill_flops(c5["lens_q"], c5["lens_kv"], hq, 64)
     tf5 = fl5 / (t["ragged_prefill"] * 1e-3) / 1e12
@@ -265,6 +280,7 @@ def main():
         "decode": {"workload": c3["name"], "splits": s3,
                    "us_decode": round(t["decode"] * 1e3, 2),
                    "us_merge": round(t["decode_merge"] * 1e3, 2),
+                   "us_decode_merge": round(tb["decode"] * 1e3, 2),
                    "bytes": b3["total"], "GB/s": round(gbs3, 1),
                    "frac": round(gbs3 / PEAK_HBM_GBS, 4),
                    "decode_kernel_GB/s": round(gbs3_k, 1),
@@ -273,6 +289,7 @@ def main():
         "split_decode": {"workload": c4["name"], "splits": s4,
                          "us_decode": round(t["split"] * 1e3, 2),
                          "us_merge": round(t["split_merge"] * 1e3, 2),
+                         "us_decode_merge": round(tb["split"] * 1e3, 2),
                          "bytes": b4["total"], "GB/s": round(gbs4, 1),
                          "frac": round(gbs4 / PEAK_HBM_GBS, 4),
                          "decode_kernel_GB/s": round(gbs4_k, 1),
@@ -292,6 +309,7 @@ def main():
                             "splits": s6,
                             "us_split": round(t["chunked_split"] * 1e3, 2),
                             "us_merge": round(t["chunked_merge"] * 1e3, 2),
+                            "us_split_merge": round(tb["chunked_split"] * 1e3, 2),
                             "TFLOP/s_split": round(tf6s, 2),
                             "frac_split": round(tf6s / PEAK_BF16_TFLOPS, 4)},
         "ragged_prefill": {"workload": c5["name"], "flops": fl5,

@@ -1198,23 +1198,6 @@ prefill_kernel(const PrefillArgs a) {
               sacc[kb][rb], 0, 0, 0);
       }
     };
-    // O^T += V^T P^T over the 32 keys of half kb (key steps hh = 0, 1)
-    auto pv = [&](int kb) __attribute__((always_inline)) {
-      u32x4 vf[2][2];
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int db = 0; db < 2; ++db) vf[hh][db] = v_operand(kb, hh, db);
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int db = 0; db < 2; ++db)
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb)
-            acc_o[db][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8, vf[hh][db]),
-                __builtin_bit_cast(bf16x8, pf[rb][kb][hh]), acc_o[db][rb], 0, 0, 0);
-    };
     auto mask = [&](int kb) __attribute__((always_inline)) {
       if constexpr (decltype(masked)::value) {
 #pragma unroll
@@ -1319,10 +1302,12 @@ prefill_kernel(const PrefillArgs a) {
       }
     }
     end_half(0);
-    // O^T += V^T P^T of half 0: each MFMA followed by two logit pairs of half 1
+    // O^T += V^T P^T of half 0: each MFMA followed by two logit pairs of half
+    // 1; the four slots of its second key step also read the V operands of
+    // half 1 (vg[hh][db]), so that their LDS latency is hidden there
     mask(1);
     start_half();
-    u32x4 vf[2][2];
+    u32x4 vf[2][2], vg[2][2];
     vf[0][0] = v_operand(0, 0, 0);
     vf[0][1] = v_operand(0, 0, 1);
     vf[1][0] = v_operand(0, 1, 0);
@@ -1341,10 +1326,20 @@ prefill_kernel(const PrefillArgs a) {
           const int q = 2 * (4 * hh + 2 * db + rb);
           pair_p(1, q);
           pair_p(1, q + 1);
+          if (hh == 1) vg[db][rb] = v_operand(1, db, rb);  // (db, rb) as (hh, db)
           ATTN_SINK_FENCE();
         }
     end_half(1);
-    pv(1);
+    // O^T += V^T P^T of half 1
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          acc_o[db][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, vg[hh][db]), __builtin_bit_cast(bf16x8, pf[rb][1][hh]),
+              acc_o[db][rb], 0, 0, 0);
 #undef ATTN_SINK_FENCE
   };
 
