@@ -1230,13 +1230,20 @@ prefill_kernel(const PrefillArgs a) {
     // row block q / 8, key step (q / 4) % 2, register pair q % 4.
     float mneg[RB], ps[RB][4], rs[RB];
     bool slow[RB];
-    auto pair_p = [&](int kb, int q) __attribute__((always_inline)) {
+    // A slot's two pairs are exponentiated in that slot and packed and
+    // summed in the next one, so the exponentials' latency is spent under
+    // the next MFMA rather than waited on.
+    auto pair_exp = [&](int kb, int q, float* ex) __attribute__((always_inline)) {
       const int rb = q >> 3, hh = (q >> 2) & 1, e = q & 3, r = 8 * hh + 2 * e;
-      const float p0 = fast_exp2(__builtin_fmaf(sacc[kb][rb][r], qk_scale_log2, mneg[rb]));
-      const float p1 = fast_exp2(__builtin_fmaf(sacc[kb][rb][r + 1], qk_scale_log2, mneg[rb]));
-      pf[rb][kb][hh][e] = pack_bf16x2(p0, p1);
-      ps[rb][e] = hh == 0 ? p0 + p1 : ps[rb][e] + (p0 + p1);
+      ex[0] = fast_exp2(__builtin_fmaf(sacc[kb][rb][r], qk_scale_log2, mneg[rb]));
+      ex[1] = fast_exp2(__builtin_fmaf(sacc[kb][rb][r + 1], qk_scale_log2, mneg[rb]));
     };
+    auto pair_fin = [&](int kb, int q, const float* ex) __attribute__((always_inline)) {
+      const int rb = q >> 3, hh = (q >> 2) & 1, e = q & 3;
+      pf[rb][kb][hh][e] = pack_bf16x2(ex[0], ex[1]);
+      ps[rb][e] = hh == 0 ? ex[0] + ex[1] : ps[rb][e] + (ex[0] + ex[1]);
+    };
+    float ex[2][4];  // exponentials of the last two slots' pairs
     auto start_half = [&]() __attribute__((always_inline)) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) mneg[rb] = m_run[rb] == kNegInf ? 0.f : -m_run[rb];
@@ -1296,11 +1303,18 @@ prefill_kernel(const PrefillArgs a) {
             __builtin_bit_cast(bf16x8, kf[s & 1]), __builtin_bit_cast(bf16x8, qf[rb][s]),
             sacc[1][rb], 0, 0, 0);
         ATTN_SINK_FENCE();
-        pair_p(0, 2 * (2 * s + rb));
-        pair_p(0, 2 * (2 * s + rb) + 1);
+        const int j = 2 * s + rb;
+        pair_exp(0, 2 * j, &ex[j & 1][0]);
+        pair_exp(0, 2 * j + 1, &ex[j & 1][2]);
+        if (j > 0) {
+          pair_fin(0, 2 * j - 2, &ex[(j - 1) & 1][0]);
+          pair_fin(0, 2 * j - 1, &ex[(j - 1) & 1][2]);
+        }
         ATTN_SINK_FENCE();
       }
     }
+    pair_fin(0, 14, &ex[1][0]);
+    pair_fin(0, 15, &ex[1][2]);
     end_half(0);
     // O^T += V^T P^T of half 0: each MFMA followed by two logit pairs of half
     // 1; the four slots of its second key step also read the V operands of
@@ -1323,12 +1337,18 @@ prefill_kernel(const PrefillArgs a) {
               __builtin_bit_cast(bf16x8, vf[hh][db]), __builtin_bit_cast(bf16x8, pf[rb][0][hh]),
               acc_o[db][rb], 0, 0, 0);
           ATTN_SINK_FENCE();
-          const int q = 2 * (4 * hh + 2 * db + rb);
-          pair_p(1, q);
-          pair_p(1, q + 1);
+          const int j = 4 * hh + 2 * db + rb;
+          pair_exp(1, 2 * j, &ex[j & 1][0]);
+          pair_exp(1, 2 * j + 1, &ex[j & 1][2]);
+          if (j > 0) {
+            pair_fin(1, 2 * j - 2, &ex[(j - 1) & 1][0]);
+            pair_fin(1, 2 * j - 1, &ex[(j - 1) & 1][2]);
+          }
           if (hh == 1) vg[db][rb] = v_operand(1, db, rb);  // (db, rb) as (hh, db)
           ATTN_SINK_FENCE();
         }
+    pair_fin(1, 14, &ex[1][0]);
+    pair_fin(1, 15, &ex[1][2]);
     end_half(1);
     // O^T += V^T P^T of half 1
 #pragma unroll
