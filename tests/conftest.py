@@ -23,7 +23,7 @@ def gpu_available() -> bool:
 
 @pytest.fixture(scope="session")
 def lib():
-    """The HIP library binding; on a GPU machine a missing library is an error."""
+    """The HIP library binding; on a machine with a GPU a missing library is an error."""
     import gqa_attention_sinks_initialised_amd as m
     m.load_library()
     return m
