@@ -1422,6 +1422,49 @@ prefill_kernel(const PrefillArgs a) {
     }
   }
 
+  // ---- epilogue, bf16 output: the wave's 64 x 64 tile of O / d goes through
+  // 8 KB of the (now idle) staging LDS, so that each store writes 8 whole
+  // 128-byte rows (1 KB contiguous when the group is 8 heads of one token):
+  // stored straight from the MFMA layout, every store instruction touched 64
+  // rows 8 bytes at a time.  In LDS, 16-byte chunk c of row r sits at slot
+  // c ^ (r & 7).
+  constexpr bool kLdsEpilogue = DT == DT_BF16 && !SPLIT && WAVES <= 2 * NSTAGE &&
+                                BK * KROW * ES >= 8192 && kHeadDim * VROW * ES >= 8192;
+  if constexpr (kLdsEpilogue) {
+    char* ob = w < NSTAGE ? lds_k[w] : lds_v[w - NSTAGE];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const float dsum = xor_sum(d_run[rb], 32);
+      const float inv = dsum > 0.f ? 1.f / dsum : 0.f;
+      const int r = 32 * rb + col;
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          const int c = 4 * db + qd;  // dims 8c + 4g + 0..3
+          const float y0 = acc_o[db][rb][4 * qd + 0] * inv, y1 = acc_o[db][rb][4 * qd + 1] * inv;
+          const float y2 = acc_o[db][rb][4 * qd + 2] * inv, y3 = acc_o[db][rb][4 * qd + 3] * inv;
+          *reinterpret_cast<u32x2*>(ob + r * 128 + 16 * (c ^ (r & 7)) + 8 * g) =
+              u32x2{pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    const int c = lane & 7;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 8 * i + (lane >> 3);
+      const u32x4 x = *reinterpret_cast<const u32x4*>(ob + r * 128 + 16 * (c ^ (r & 7)));
+      const int tl = r / group, hl = r - tl * group;
+      const int t = t_begin + w * TW + tl;
+      if (tl < TW && t < Lq)
+        *reinterpret_cast<u32x4*>(a.out + (((size_t)q0 + t) * hq + kvh * group + hl) * kHeadDim * ES +
+                                  16 * c) = x;
+    }
+    return;
+  }
+
   // ---- epilogue: out = O / d (SPLIT: the state m, d, O of this chunk, m in
   // natural-log units), rows of this lane, dims 32db + 8qd + 4g + 0..3
 #pragma unroll
