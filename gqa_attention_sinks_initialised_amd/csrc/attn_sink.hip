@@ -644,6 +644,14 @@ template <int DT, int RB, int WAVES, bool PAGED, bool SPLIT>
 __global__ __launch_bounds__(64 * WAVES, (PrefillCfg<DT, RB, WAVES>::MIN_WAVES_PER_EU)) void
 prefill_kernel(const PrefillArgs a) {
   using Cfg = PrefillCfg<DT, RB, WAVES>;
+  // Every argument is needed in the prologue: this (pure, so not a memory
+  // barrier) empty asm makes them load in one batch here, not in dependent
+  // rounds along the branches below.
+  int args_ready;
+  asm("" : "=s"(args_ready)
+      : "s"(a.q), "s"(a.k), "s"(a.v), "s"(a.sinks), "s"(a.cu_q), "s"(a.cu_kv), "s"(a.out),
+        "s"(a.total_q), "s"(a.total_kv), "s"(a.hkv), "s"(a.group), "s"(a.n_qtiles), "s"(a.n_pairs),
+        "s"(a.rank_seqs), "s"(a.seq_major), "s"(a.qk_scale_log2));
   const char* __restrict__ q = a.q;
   const char* __restrict__ k = a.k;
   const char* __restrict__ v = a.v;
@@ -738,15 +746,20 @@ prefill_kernel(const PrefillArgs a) {
     k0 = __builtin_amdgcn_readlane(lk0, b);
     Lkv = __builtin_amdgcn_readlane(lk1, b) - k0;
   } else {
-    q0 = clampi(a.cu_q[b], 0, total_q);
-    q1 = clampi(a.cu_q[b + 1], q0, total_q);
+    // the sequence's four bounds, loaded together
+    const int cq0 = a.cu_q[b], cq1 = a.cu_q[b + 1];
+    const int ck0 = PAGED ? 0 : a.cu_kv[b], ck1 = PAGED ? a.kv_lens[b] : a.cu_kv[b + 1];
+    asm("" : "=s"(args_ready) : "s"(cq0), "s"(cq1), "s"(ck0), "s"(ck1), "s"(args_ready));
+    q0 = clampi(cq0, 0, total_q);
+    q1 = clampi(cq1, q0, total_q);
     if constexpr (PAGED) {
-      Lkv = clampi(a.kv_lens[b], 0, a.max_pages * kPage);
+      Lkv = clampi(ck1, 0, a.max_pages * kPage);
     } else {
-      k0 = clampi(a.cu_kv[b], 0, a.total_kv);
-      Lkv = clampi(a.cu_kv[b + 1], k0, a.total_kv) - k0;
+      k0 = clampi(ck0, 0, a.total_kv);
+      Lkv = clampi(ck1, k0, a.total_kv) - k0;
     }
   }
+  asm volatile("" ::"s"(args_ready));
   const int Lq = q1 - q0;
   const int t_begin = tile * TB;
   if (t_begin >= Lq) return;
