@@ -252,3 +252,28 @@ def test_decode_c4_sampled_matches_oracle(lib):
     gd = pd.cpu()[torch.as_tensor(rb).long(), torch.as_tensor(rh).long()].double().numpy()
     np.testing.assert_allclose(gm, rm, rtol=1e-5, atol=1e-5)
     np.testing.assert_allclose(gd, rd, rtol=1e-2)
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+def test_decode_pages_past_4gib(lib, splits):
+    """Pages may sit anywhere in caches larger than 4 GiB: the result is bit
+    for bit that of the compact cache holding the same logical pages."""
+    d = _to_dev(workloads.decode_inputs([37, 300, 1], hq=8, hkv=2, dtype=torch.bfloat16,
+                                        seed=91, sink_std=1.5))
+    small, _ = run_decode(lib, d, splits)
+    kc, vc, pt = d["k_cache"], d["v_cache"], d["page_table"]
+    block = kc[0].numel() * kc.element_size()
+    nbig = -(-(5 << 30) // block)
+    big = dict(d)
+    big["k_cache"] = torch.empty((nbig,) + tuple(kc.shape[1:]), dtype=kc.dtype, device=DEV)
+    big["v_cache"] = torch.empty((nbig,) + tuple(vc.shape[1:]), dtype=vc.dtype, device=DEV)
+    n = kc.shape[0]
+    new_ids = nbig - 1 - torch.arange(n, device=DEV)
+    big["k_cache"][new_ids] = kc
+    big["v_cache"][new_ids] = vc
+    valid = (pt >= 0) & (pt < n)
+    big["page_table"] = torch.where(valid, nbig - 1 - pt, pt).to(torch.int32)
+    assert int(big["page_table"][valid].min()) * block >= (4 << 30)
+    out, _ = run_decode(lib, big, splits)
+    torch.cuda.synchronize()
+    assert torch.equal(out.cpu().view(torch.int16), small.cpu().view(torch.int16))
