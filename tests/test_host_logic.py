@@ -22,3 +22,25 @@ def test_prefill_splits():
     assert m.default_prefill_splits(1, 1, 8, 16, 600) == 2
     assert m.default_prefill_splits(1, 1, 8, 16, 100) == 1
     assert m.default_prefill_splits(0, 8, 8, 0, 0) == 1
+
+
+def test_bench_flop_count_matches_enumeration():
+    """The benchmark's algorithmic flops (4 * D per visible (query, key) pair
+    per head) against an explicit enumeration of the visible pairs, causal
+    rows aligned bottom-right."""
+    import itertools
+    import random
+
+    import bench
+
+    rng = random.Random(7)
+    for _ in range(20):
+        b = rng.randint(1, 4)
+        lq = [rng.randint(0, 40) for _ in range(b)]
+        lkv = [rng.randint(0, 60) for _ in range(b)]
+        for causal in (True, False):
+            pairs = 0
+            for q_len, k_len in zip(lq, lkv):
+                for i, j in itertools.product(range(q_len), range(k_len)):
+                    pairs += (not causal) or j <= i + (k_len - q_len)
+            assert bench.prefill_flops(lq, lkv, 3, 64, causal) == 4 * 64 * 3 * pairs
