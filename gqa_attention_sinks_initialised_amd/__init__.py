@@ -248,6 +248,7 @@ def attn_sink_decode_paged(q, k_cache, v_cache, page_table, kv_lens, sinks,
     _need(k_cache.dim() == 4 and v_cache.dim() == 4, "caches must be 4-d")
     num_pages, hkv, page, dim = k_cache.shape
     _need(v_cache.shape == (num_pages, hkv, dim, page), "v_cache must be [pages, Hkv, D, P]")
+    _need(q.dim() == 3 and q.shape[2] == dim, "q must be [B, Hkv*G, D] with the caches' D")
     batch, hq = q.shape[0], q.shape[1]
     _need(hq == hkv * group_size, "q heads != kv heads * group_size")
     _need(page_table.dim() == 2 and page_table.shape[0] == batch, "bad page_table")
@@ -256,17 +257,13 @@ def attn_sink_decode_paged(q, k_cache, v_cache, page_table, kv_lens, sinks,
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(dim)
     S = int(num_splits)
+    _need(S >= 1, "num_splits must be >= 1")
     if S == 1:
         if out is None:
             out = torch.empty_like(q)
+        _need(out.shape == q.shape and out.dtype == q.dtype, "bad out tensor")
     else:
-        f32 = dict(device=q.device, dtype=torch.float32)
-        if partial_m is None:
-            partial_m = torch.empty((batch, hq, S), **f32)
-        if partial_d is None:
-            partial_d = torch.empty((batch, hq, S), **f32)
-        if partial_o is None:
-            partial_o = torch.empty((batch, hq, S, dim), **f32)
+        partial_m, partial_d, partial_o = _partials(q, S, partial_m, partial_d, partial_o)
     rc = load_library().attn_sink_decode_paged(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table), _ptr(kv_lens), _ptr(sinks),
         batch, page_table.shape[1], num_pages, hkv, int(group_size), dim, page,
@@ -280,13 +277,18 @@ def attn_sink_merge(partial_m, partial_d, partial_o, out=None, out_dtype=None, s
     """Merge split states: m, d [B, Hq, S], o [B, Hq, S, 64] fp32 -> [B, Hq, 64]."""
     import torch
     _dev(partial_m, partial_d, partial_o, out)
+    _need(partial_m.dim() == 3 and partial_o.dim() == 4, "bad partial shapes")
     batch, hq, S = partial_m.shape
     dim = partial_o.shape[-1]
     _need(partial_d.shape == partial_m.shape and partial_o.shape == (batch, hq, S, dim),
           "bad partial shapes")
+    _need(all(t.dtype == torch.float32 for t in (partial_m, partial_d, partial_o)),
+          "partials must be float32")
     if out is None:
         out = torch.empty((batch, hq, dim), device=partial_m.device,
                           dtype=out_dtype or torch.bfloat16)
+    _need(out.shape == (batch, hq, dim), "out must be [B, Hq, D]")
+    _need(out_dtype is None or out.dtype == out_dtype, "out dtype differs from out_dtype")
     rc = load_library().attn_sink_merge(
         _ptr(partial_m), _ptr(partial_d), _ptr(partial_o), batch, hq, S, dim,
         _dtype_code(out), _ptr(out), _stream(stream))

@@ -1,6 +1,4 @@
 """Shared comparison helpers for the parity tests (no attention arithmetic)."""
-import math
-
 import numpy as np
 import torch
 
@@ -43,24 +41,3 @@ def assert_close(got, ref, dtype, what=""):
                              "first %s; %s" % (what, int(bad.sum()), bad.size, atol, rtol,
                                                idx, report(g, r)))
     return report(g, r)
-
-
-def sample_prefill_rows(lens_q, hq, n_per_seq, seed):
-    """(tokens, heads) rows covering the first and last token of every sequence
-    plus random ones."""
-    g = np.random.default_rng(seed)
-    toks, heads = [], []
-    off = 0
-    for L in lens_q:
-        if L == 0:
-            continue
-        picks = [0, L - 1] + list(g.integers(0, L, size=max(0, n_per_seq - 2)))
-        for t in picks:
-            toks.append(off + int(t))
-            heads.append(int(g.integers(0, hq)))
-        off += L
-    return np.array(toks, dtype=np.int64), np.array(heads, dtype=np.int32)
-
-
-def finite_cut(x):
-    return x if math.isfinite(x) else (-1e30 if x < 0 else 1e30)

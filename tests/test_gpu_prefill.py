@@ -1,23 +1,25 @@
 """GPU parity of ragged (causal) prefill with sinks (MI355X)."""
 import math
 
-import numpy as np
 import pytest
 import torch
 
 import oracle
 import workloads
-from helpers import assert_close, sample_prefill_rows
+from helpers import assert_close
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
 def run_prefill(lib, d, causal=True):
+    """Prefill through the C ABI into an output pre-filled with NaN, so that
+    any element the grid never writes fails the comparison."""
     dd = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
-    out = lib.attn_sink_prefill(dd["q"], dd["k"], dd["v"], dd["sinks"], dd["cu_seqlens_q"],
-                                dd["cu_seqlens_kv"], max(d["lens_q"] + [0]), d["group"],
-                                d["sm_scale"], causal)
+    out = torch.full_like(dd["q"], float("nan"))
+    lib.attn_sink_prefill(dd["q"], dd["k"], dd["v"], dd["sinks"], dd["cu_seqlens_q"],
+                          dd["cu_seqlens_kv"], max(d["lens_q"] + [0]), d["group"],
+                          d["sm_scale"], causal, out=out)
     torch.cuda.synchronize()
     return out.cpu()
 
@@ -116,26 +118,20 @@ def test_prefill_deterministic(lib):
     assert torch.equal(run_prefill(lib, d), run_prefill(lib, d))
 
 
-def test_prefill_c2_sampled_matches_oracle(lib):
-    """Causal prefill workload B=4 x 2048, 64/8 heads, bf16: sampled rows."""
+def test_prefill_c2_full_matches_oracle(lib):
+    """Causal prefill workload B=4 x 2048, 64/8 heads, bf16: every element of
+    the output against the fp64 oracle (about 5 s of oracle time on 16 host
+    cores)."""
     d = workloads.workload(2)
     out = run_prefill(lib, d)
-    toks, heads = sample_prefill_rows(d["lens_q"], 64, 96, seed=2)
-    ref = oracle_prefill(d, rows=(toks, heads))
-    got = out[torch.as_tensor(toks), torch.as_tensor(heads).long()]
-    assert_close(got, ref, torch.bfloat16, "C2 sampled")
-    assert torch.all(torch.isfinite(out.float()))
+    assert_close(out, oracle_prefill(d), torch.bfloat16, "C2 full")
 
 
-def test_prefill_c5_sampled_matches_oracle(lib):
+def test_prefill_c5_full_matches_oracle(lib):
     """Ragged edge-case workload (16 sequences, len U[128,4096], sinks
-    {-inf, 0, N(0,1), +20}, logits up to about +-30): sampled rows cover
-    every (sink category, Q multiplier) head class."""
+    {-inf, 0, N(0,1), +20}, logits up to about +-30), the launch the benchmark
+    times (sequence-major order per XCD): every element against the fp64
+    oracle (about 26 s of oracle time on 16 host cores)."""
     d = workloads.workload(5)
     out = run_prefill(lib, d)
-    toks, _ = sample_prefill_rows(d["lens_q"], 64, 24, seed=5)
-    heads = np.arange(len(toks), dtype=np.int32) % 64
-    ref = oracle_prefill(d, rows=(toks, heads))
-    got = out[torch.as_tensor(toks), torch.as_tensor(heads).long()]
-    assert_close(got, ref, torch.bfloat16, "C5 sampled")
-    assert torch.all(torch.isfinite(out.float()))
+    assert_close(out, oracle_prefill(d), torch.bfloat16, "C5 full")

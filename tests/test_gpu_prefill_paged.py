@@ -19,7 +19,7 @@ import torch
 
 import oracle
 import workloads
-from helpers import assert_close, sample_prefill_rows, tol_for
+from helpers import assert_close, tol_for
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -40,12 +40,25 @@ def paged_case(lens_q, lens_kv, hq, hkv, dtype, seed, fill=NAN, **kw):
     return d
 
 
+def _nan_outputs(q, splits, partials=False):
+    """Output (splits == 1), or split partial buffers, pre-filled with NaN so
+    that any element the grid never writes fails the comparison."""
+    nan = float("nan")
+    if splits == 1 and not partials:
+        return dict(out=torch.full_like(q, nan))
+    rows, hq, dim = q.shape
+    f32 = dict(device=q.device, dtype=torch.float32)
+    return dict(partial_m=torch.full((rows, hq, splits), nan, **f32),
+                partial_d=torch.full((rows, hq, splits), nan, **f32),
+                partial_o=torch.full((rows, hq, splits, dim), nan, **f32))
+
+
 def run_paged(lib, d, causal=True, splits=1):
     dd = _dev(d)
     r = lib.attn_sink_prefill_paged(dd["q"], dd["k_cache"], dd["v_cache"], dd["page_table"],
                                     dd["cu_seqlens_q"], dd["kv_lens"], dd["sinks"],
                                     max(d["lens_q"] + [0]), d["group"], d["sm_scale"], causal,
-                                    num_splits=splits)
+                                    num_splits=splits, **_nan_outputs(dd["q"], splits))
     torch.cuda.synchronize()
     return r.cpu() if splits == 1 else tuple(t.cpu() for t in r)
 
@@ -55,7 +68,8 @@ def run_ragged_partials(lib, d, causal, splits):
     r = lib.attn_sink_prefill_partials(dd["q"], dd["k"], dd["v"], dd["sinks"],
                                        dd["cu_seqlens_q"], dd["cu_seqlens_kv"],
                                        max(d["lens_q"] + [0]), d["group"], splits,
-                                       d["sm_scale"], causal)
+                                       d["sm_scale"], causal,
+                                       **_nan_outputs(dd["q"], splits, partials=True))
     torch.cuda.synchronize()
     return tuple(t.cpu() for t in r)
 
@@ -230,23 +244,22 @@ def test_paged_prefill_deterministic(lib):
     assert all(torch.equal(x, y) for x, y in zip(a, b))
 
 
-def test_chunked_prefill_long_cache_sampled(lib):
-    """Chunked prefill at serving size: 4 sequences, 512 new tokens each on
-    top of 15872 cached ones (kv_len 16384), Hq 64 / Hkv 8, bf16, split 8
-    ways and unsplit; sampled rows against the oracle."""
-    lens_q, lens_kv = [512] * 4, [16384] * 4
-    d = paged_case(lens_q, lens_kv, 64, 8, torch.bfloat16, seed=77, fill=0.0,
-                   sink_std=math.sqrt(2.0))
-    toks, heads = sample_prefill_rows(lens_q, 64, 24, seed=6)
-    ref = oracle_paged(d, True, rows=(toks, heads))
-    idx = (torch.as_tensor(toks), torch.as_tensor(heads).long())
-    out = run_paged(lib, d)
-    assert_close(out[idx], ref, torch.bfloat16, "chunked prefill unsplit")
-    pm, pd, po = run_paged(lib, d, True, 8)
-    merged = lib.attn_sink_merge(pm.to(DEV), pd.to(DEV), po.to(DEV))
+def test_chunked_prefill_workload_full(lib):
+    """The benchmark's chunked prefill: one sequence, 512 new tokens on a
+    paged cache of 32768 keys (the new tokens' included), Hq 64 / Hkv 8,
+    bf16, random page placement; unsplit, and split as the benchmark splits
+    it then merged.  Every output element, and every partial state through
+    m + ln d and o / d, against the fp64 oracle (about 20 s of oracle time on
+    16 host cores)."""
+    from gqa_attention_sinks_initialised_amd import default_prefill_splits
+    d = workloads.workload(6)
+    S = default_prefill_splits(1, 8, 8, 512, 32768)
+    ref = oracle_paged(d, True)
+    assert_close(run_paged(lib, d), ref, torch.bfloat16, "chunked prefill unsplit")
+    got = run_paged(lib, d, True, S)
+    merged = torch.full_like(_dev(d)["q"], NAN)
+    lib.attn_sink_merge(*(t.to(DEV) for t in got), out=merged, out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
-    assert_close(merged.cpu()[idx], ref, torch.bfloat16, "chunked prefill split 8")
-    rm, rd, ro = oracle_paged(d, True, 8, rows=(toks, heads))
-    check_partials((pm[idx].unsqueeze(0), pd[idx].unsqueeze(0), po[idx].unsqueeze(0)),
-                   (rm[None], rd[None], ro[None]), torch.bfloat16, d["sinks"][heads][None],
+    assert_close(merged.cpu(), ref, torch.bfloat16, "chunked prefill split %d" % S)
+    check_partials(got, oracle_paged(d, True, S), torch.bfloat16, d["sinks"][None, :],
                    "chunked prefill partials")
