@@ -24,6 +24,7 @@ import argparse
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -77,6 +78,35 @@ def counted_traffic():
         return None
     return {k: v.get("fetch_bytes", 0.0) + v.get("write_bytes", 0.0)
             for k, v in rec.get("per_launch_bytes", {}).items()}
+
+
+def profiled_clock():
+    """Average shader clock (GHz) per kernel under its own load, from a
+    rocprofv3 counter pass: GRBM_GUI_ACTIVE summed over the 8 XCDs, divided
+    by 8 and by the dispatch's traced duration.  Kept in profiles/clock.json
+    with the hash of the kernel source it was taken on; None once the kernels
+    have changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "clock.json")
+    src = os.path.join(ROOT, "gqa_attention_sinks_initialised_amd", "csrc", "attn_sink.hip")
+    try:
+        rec = json.load(open(path))
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != sha:
+        return None
+    return rec.get("clock_ghz")
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def main():
@@ -208,6 +238,8 @@ def main():
             evs[len(ops)].record()
 
     def timed(n, split_pairs):
+        """Mean bracket time (ms) of every op that opens a bracket, the
+        per-step samples of each, and the wall time of the n steps."""
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(ops) + 1)]
                for _ in range(n)]
         torch.cuda.synchronize()
@@ -216,13 +248,13 @@ def main():
             step(evs[i], split_pairs)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        # bracket time (ms) of every op that opens a bracket
         marks = [i for i, op in enumerate(ops) if split_pairs or not op[2]] + [len(ops)]
-        t = {}
+        t, samples = {}, {}
         for a, b in zip(marks, marks[1:]):
             if not ops[a][0].startswith("_"):
-                t[ops[a][0]] = sum(e[a].elapsed_time(e[b]) for e in evs) / n
-        return t, wall
+                samples[ops[a][0]] = [e[a].elapsed_time(e[b]) for e in evs]
+                t[ops[a][0]] = sum(samples[ops[a][0]]) / n
+        return t, samples, wall
 
     for _ in range(args.warmup):
         step()
@@ -230,10 +262,17 @@ def main():
 
     # The K timed steps; then a few more with an event between every launch,
     # for the per-kernel split of each decode + merge bracket.
-    tb, wall = timed(args.steps, False)
-    t, _ = timed(min(args.steps, 10), True)
+    tb, sb, wall = timed(args.steps, False)
+    t, _, _ = timed(min(args.steps, 10), True)
     for name in ("prefill", "paged_prefill", "chunked", "ragged_prefill"):
         t[name] = tb[name]
+
+    def spread(name):
+        """Mean, median and min of one bracket over the K timed steps (us)."""
+        x = sorted(sb[name])
+        return {"us_mean": round(tb[name] * 1e3, 2),
+                "us_median": round(statistics.median(x) * 1e3, 2),
+                "us_min": round(x[0] * 1e3, 2)}
 
     fl2 = prefill_flops(c2["lens_q"], c2["lens_kv"], hq, 64)
     tflops = fl2 / (t["prefill"] * 1e-3) / 1e12
@@ -254,6 +293,8 @@ def main():
     tf5 = fl5 / (t["ragged_prefill"] * 1e-3) / 1e12
 
     traffic = counted_traffic() or {}
+    clock = profiled_clock() or {}
+    clk2 = clock.get("prefill")
     result = {
         "metric": "prefill attention TFLOP/s (bf16) + decode KV-read HBM GB/s, % of roofline",
         "value": round(tflops, 2),
@@ -276,11 +317,17 @@ def main():
                      "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic.get("prefill"),
                      "kernel": "prefill_kernel<bf16>", "flops_per_launch": fl2,
-                     "us_per_launch": round(t["prefill"] * 1e3, 2)},
+                     "us_per_launch": round(t["prefill"] * 1e3, 2),
+                     **spread("prefill"),
+                     "clock_ghz": clk2,
+                     "frac_at_clock": (round(tflops / (PEAK_BF16_TFLOPS * clk2 / 2.4), 4)
+                                       if clk2 else None)},
         "decode": {"workload": c3["name"], "splits": s3,
                    "us_decode": round(t["decode"] * 1e3, 2),
                    "us_merge": round(t["decode_merge"] * 1e3, 2),
                    "us_decode_merge": round(tb["decode"] * 1e3, 2),
+                   "decode_merge": spread("decode"),
+                   "clock_ghz": clock.get("decode_paged"),
                    "bytes": b3["total"], "GB/s": round(gbs3, 1),
                    "frac": round(gbs3 / PEAK_HBM_GBS, 4),
                    "decode_kernel_GB/s": round(gbs3_k, 1),
@@ -290,6 +337,8 @@ def main():
                          "us_decode": round(t["split"] * 1e3, 2),
                          "us_merge": round(t["split_merge"] * 1e3, 2),
                          "us_decode_merge": round(tb["split"] * 1e3, 2),
+                         "decode_merge": spread("split"),
+                         "clock_ghz": clock.get("decode_split"),
                          "bytes": b4["total"], "GB/s": round(gbs4, 1),
                          "frac": round(gbs4 / PEAK_HBM_GBS, 4),
                          "decode_kernel_GB/s": round(gbs4_k, 1),
@@ -299,6 +348,7 @@ def main():
                                       "and values from a paged cache (16-token pages, random "
                                       "placement)",
                           "us": round(t["paged_prefill"] * 1e3, 2),
+                          **spread("paged_prefill"),
                           "TFLOP/s": round(tf2p, 2),
                           "frac": round(tf2p / PEAK_BF16_TFLOPS, 4),
                           "traffic": traffic.get("paged_prefill")},
@@ -314,6 +364,8 @@ def main():
                             "frac_split": round(tf6s / PEAK_BF16_TFLOPS, 4)},
         "ragged_prefill": {"workload": c5["name"], "flops": fl5,
                            "us": round(t["ragged_prefill"] * 1e3, 2),
+                           **spread("ragged_prefill"),
+                           "clock_ghz": clock.get("ragged_prefill"),
                            "TFLOP/s": round(tf5, 2),
                            "frac": round(tf5 / PEAK_BF16_TFLOPS, 4),
                            "traffic": traffic.get("ragged_prefill")},
@@ -375,7 +427,7 @@ def cpu_baseline(c2, target_s):
         "%d query tokens x 64 heads of the prefill workload (evenly spaced over the 4 "
         "sequences)" % (len(toks) // hq))
     return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.max_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": "%s, %.3g GFLOP algorithmic, %.1f s" % (what, fl / 1e9, dt)}
 
 

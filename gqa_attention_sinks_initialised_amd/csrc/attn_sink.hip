@@ -640,9 +640,14 @@ __device__ __forceinline__ u32x4 keep_first(u32x4 x, int n, int es) {
   return x;
 }
 
-template <int DT, int RB, int WAVES, bool PAGED, bool SPLIT>
+// WIDE (paged caches of 4 GiB or more): each page block is read through its
+// own buffer resource, built in scalar registers from the block's 64-bit
+// address (page ids are wave-uniform), instead of at a 32-bit offset from
+// the cache base.
+template <int DT, int RB, int WAVES, bool PAGED, bool SPLIT, bool WIDE = false>
 __global__ __launch_bounds__(64 * WAVES, (PrefillCfg<DT, RB, WAVES>::MIN_WAVES_PER_EU)) void
 prefill_kernel(const PrefillArgs a) {
+  static_assert(PAGED || !WIDE, "only paged caches take 64-bit page bases");
   using Cfg = PrefillCfg<DT, RB, WAVES>;
   // Every argument is needed in the prologue: this (pure, so not a memory
   // barrier) empty asm makes them load in one batch here, not in dependent
@@ -919,9 +924,16 @@ prefill_kernel(const PrefillArgs a) {
         const int id = ids[u];
         // pages past the sequence and bad ids (outside [0, num_pages)) are skipped
         if (page_of(jt, u) * kPage < Lkv && id >= 0 && id < a.num_pages) {
-          const uint32_t base = ((uint32_t)id * hkv + kvh) * kBlock;
-          stk[u] = buf_load16(kr, 16 * vrem, base);
-          stv[u][0] = buf_load16(vr, 16 * vrem, base);
+          if constexpr (WIDE) {
+            // one buffer resource per page block, built in scalar registers
+            const size_t base = ((size_t)id * hkv + kvh) * kBlock;
+            stk[u] = buf_load16(make_rsrc(k + base, kBlock), 16 * vrem);
+            stv[u][0] = buf_load16(make_rsrc(v + base, kBlock), 16 * vrem);
+          } else {
+            const uint32_t base = ((uint32_t)id * hkv + kvh) * kBlock;
+            stk[u] = buf_load16(kr, 16 * vrem, base);
+            stv[u][0] = buf_load16(vr, 16 * vrem, base);
+          }
           // slots of the sequence's last page past its last key: zero V (their
           // scores are masked, and 0 * junk must not reach O)
           if (key0 + (tp + 1) * kPage > Lkv)
@@ -1547,7 +1559,7 @@ constexpr int kDecodeUnroll = ATTN_SINK_DECODE_UNROLL;
 
 // Launch the prefill kernel for (dtype, key source, output form): a 1-D grid
 // of query tiles x (sequence, kv head) pairs x key chunks.
-template <bool PAGED, bool SPLIT>
+template <bool PAGED, bool SPLIT, bool WIDE = false>
 int launch_prefill(PrefillArgs a, int dtype, int batch, int max_seqlen_q, hipStream_t s) {
   if ((int64_t)batch * a.hkv > INT32_MAX) return ATTN_SINK_ERR_UNSUPPORTED;
   a.n_pairs = batch * a.hkv;
@@ -1564,9 +1576,10 @@ int launch_prefill(PrefillArgs a, int dtype, int batch, int max_seqlen_q, hipStr
   if (blocks > INT32_MAX) return ATTN_SINK_ERR_UNSUPPORTED;
   const dim3 grid((unsigned)blocks);
   if (dtype == ATTN_SINK_F32)
-    hipLaunchKernelGGL((prefill_kernel<DT_F32, 2, 4, PAGED, SPLIT>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((prefill_kernel<DT_F32, 2, 4, PAGED, SPLIT, WIDE>), grid, dim3(256), 0, s,
+                       a);
   else
-    hipLaunchKernelGGL((prefill_kernel<DT_BF16, 2, kPrefillWaves, PAGED, SPLIT>), grid,
+    hipLaunchKernelGGL((prefill_kernel<DT_BF16, 2, kPrefillWaves, PAGED, SPLIT, WIDE>), grid,
                        dim3(64 * kPrefillWaves), 0, s, a);
   return launch_status();
 }
@@ -1645,6 +1658,100 @@ int attn_sink_prefill_partials_impl(const void* q, const void* k, const void* v,
             : launch_prefill<false, false>(a, dtype, batch, max_seqlen_q, s);
 }
 
+// Checks of the decode arguments other than the output buffers.
+int check_decode_args(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* page_table, const int32_t* kv_lens, const float* sinks,
+                      int batch, int max_pages_per_seq, int num_pages, int num_kv_heads,
+                      int group_size, int head_dim, int page_size, float sm_scale, int dtype,
+                      int num_splits) {
+  // the caches may be NULL only when they hold no page
+  if (!q || !page_table || !kv_lens || !sinks || ((!k_cache || !v_cache) && num_pages != 0))
+    return ATTN_SINK_ERR_INVALID_ARG;
+  if (num_splits < 1) return ATTN_SINK_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(page_table, 4) || !aligned(kv_lens, 4) || !aligned(sinks, 4))
+    return ATTN_SINK_ERR_INVALID_ARG;
+  if (batch < 0 || max_pages_per_seq < 1 || num_pages < 0 || num_kv_heads < 1 ||
+      group_size < 1 || head_dim < 1 || page_size < 1 ||
+      (dtype != ATTN_SINK_F32 && dtype != ATTN_SINK_BF16) || !finite_positive(sm_scale))
+    return ATTN_SINK_ERR_INVALID_ARG;
+  if (head_dim != kHeadDim || page_size != kPage || group_size > 16)
+    return ATTN_SINK_ERR_UNSUPPORTED;
+  if (batch > 65535 || num_kv_heads > 65535 ||
+      (int64_t)max_pages_per_seq * kPage > INT32_MAX ||
+      (int64_t)num_splits * max_pages_per_seq > INT32_MAX)
+    return ATTN_SINK_ERR_UNSUPPORTED;
+  return ATTN_SINK_OK;
+}
+
+int decode_paged_impl(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* page_table, const int32_t* kv_lens, const float* sinks,
+                      int batch, int max_pages_per_seq, int num_pages, int num_kv_heads,
+                      int group_size, int head_dim, int page_size, float sm_scale, int dtype,
+                      int num_splits, float* partial_m, float* partial_d, float* partial_o,
+                      void* out, void* stream) {
+  const int rc = check_decode_args(q, k_cache, v_cache, page_table, kv_lens, sinks, batch,
+                                   max_pages_per_seq, num_pages, num_kv_heads, group_size,
+                                   head_dim, page_size, sm_scale, dtype, num_splits);
+  if (rc != ATTN_SINK_OK) return rc;
+  if (num_splits == 1 && !out) return ATTN_SINK_ERR_INVALID_ARG;
+  if (num_splits > 1 && (!partial_m || !partial_d || !partial_o)) return ATTN_SINK_ERR_INVALID_ARG;
+  if ((out && !aligned(out, 16)) || (partial_m && !aligned(partial_m, 4)) ||
+      (partial_d && !aligned(partial_d, 4)) || (partial_o && !aligned(partial_o, 16)))
+    return ATTN_SINK_ERR_INVALID_ARG;
+  if (batch == 0) return ATTN_SINK_OK;
+  const dim3 grid(num_splits, num_kv_heads, batch);
+  const float qk = sm_scale * kLog2e;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (dtype == ATTN_SINK_BF16)
+    hipLaunchKernelGGL((decode_kernel<DT_BF16, kDecodeWaves, kDecodeUnroll>), grid,
+                       dim3(64 * kDecodeWaves), 0, s, (const char*)q, (const char*)k_cache,
+                       (const char*)v_cache, page_table, kv_lens, sinks, max_pages_per_seq,
+                       num_pages, num_kv_heads, group_size, qk, num_splits, partial_m,
+                       partial_d, partial_o, (char*)out);
+  else
+    hipLaunchKernelGGL((decode_kernel<DT_F32, kDecodeWaves, kDecodeUnroll>), grid,
+                       dim3(64 * kDecodeWaves), 0, s, (const char*)q, (const char*)k_cache,
+                       (const char*)v_cache, page_table, kv_lens, sinks, max_pages_per_seq,
+                       num_pages, num_kv_heads, group_size, qk, num_splits, partial_m,
+                       partial_d, partial_o, (char*)out);
+  return launch_status();
+}
+
+int merge_impl(const float* partial_m, const float* partial_d, const float* partial_o,
+               int batch, int num_q_heads, int num_splits, int head_dim, int out_dtype,
+               void* out, void* stream) {
+  if (!partial_m || !partial_d || !partial_o || !out) return ATTN_SINK_ERR_INVALID_ARG;
+  if (!aligned(partial_m, 4) || !aligned(partial_d, 4) || !aligned(partial_o, 16) ||
+      !aligned(out, 16))
+    return ATTN_SINK_ERR_INVALID_ARG;
+  if (batch < 0 || num_q_heads < 1 || num_splits < 1 || head_dim < 1 ||
+      (out_dtype != ATTN_SINK_F32 && out_dtype != ATTN_SINK_BF16))
+    return ATTN_SINK_ERR_INVALID_ARG;
+  if (head_dim != kHeadDim) return ATTN_SINK_ERR_UNSUPPORTED;
+  const int64_t rows = (int64_t)batch * num_q_heads;
+  if (rows > INT32_MAX - 16) return ATTN_SINK_ERR_UNSUPPORTED;
+  if (rows == 0) return ATTN_SINK_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const bool bf = out_dtype == ATTN_SINK_BF16;
+  // chunk lanes per row: up to 16, fewer when there are fewer splits
+  const int cl = num_splits >= 16 ? 16 : num_splits >= 8 ? 8 : num_splits >= 4 ? 4 : 2;
+  const int rpb = 256 / (16 * cl);
+  const dim3 grid((unsigned)((rows + rpb - 1) / rpb));
+#define ATTN_SINK_MERGE(CLV)                                                                  \
+  hipLaunchKernelGGL((bf ? merge_kernel<DT_BF16, CLV> : merge_kernel<DT_F32, CLV>), grid,      \
+                     dim3(256), 0, s, partial_m, partial_d, partial_o, (int)rows, num_splits,  \
+                     (char*)out)
+  switch (cl) {
+    case 16: ATTN_SINK_MERGE(16); break;
+    case 8: ATTN_SINK_MERGE(8); break;
+    case 4: ATTN_SINK_MERGE(4); break;
+    default: ATTN_SINK_MERGE(2); break;
+  }
+#undef ATTN_SINK_MERGE
+  return launch_status();
+}
+
 }  // namespace
 
 extern "C" {
@@ -1712,9 +1819,11 @@ int attn_sink_prefill_paged(const void* q, const void* k_cache, const void* v_ca
   if (page_size != kPage) return ATTN_SINK_ERR_UNSUPPORTED;
   const int es = dtype == ATTN_SINK_BF16 ? 2 : 4;
   const int64_t cache_bytes = (int64_t)num_pages * num_kv_heads * kPage * kHeadDim * es;
-  if (cache_bytes >= (int64_t)1 << 32 ||
-      (int64_t)max_pages_per_seq * kPage + (int64_t)kPage * num_splits > INT32_MAX)
+  if ((int64_t)max_pages_per_seq * kPage + (int64_t)kPage * num_splits > INT32_MAX)
     return ATTN_SINK_ERR_UNSUPPORTED;
+  // caches below 4 GiB: pages at 32-bit offsets from the cache base (buffer
+  // loads); larger caches: 64-bit page bases
+  const bool wide = cache_bytes >= (int64_t)1 << 32;
   if (batch == 0 || total_q == 0 || max_seqlen_q == 0) return ATTN_SINK_OK;
   PrefillArgs a{};
   a.q = (const char*)q;
@@ -1735,9 +1844,12 @@ int attn_sink_prefill_paged(const void* q, const void* k_cache, const void* v_ca
   a.splits = num_splits;
   a.max_pages = max_pages_per_seq;
   a.num_pages = num_pages;
-  a.cache_bytes = (uint32_t)cache_bytes;
+  a.cache_bytes = wide ? 0u : (uint32_t)cache_bytes;
   a.qk_scale_log2 = sm_scale * kLog2e;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (wide)
+    return num_splits == 1 ? launch_prefill<true, false, true>(a, dtype, batch, max_seqlen_q, s)
+                           : launch_prefill<true, true, true>(a, dtype, batch, max_seqlen_q, s);
   return num_splits == 1 ? launch_prefill<true, false>(a, dtype, batch, max_seqlen_q, s)
                          : launch_prefill<true, true>(a, dtype, batch, max_seqlen_q, s);
 }
@@ -1748,78 +1860,17 @@ int attn_sink_decode_paged(const void* q, const void* k_cache, const void* v_cac
                            int group_size, int head_dim, int page_size, float sm_scale,
                            int dtype, int num_splits, float* partial_m, float* partial_d,
                            float* partial_o, void* out, void* stream) {
-  // the caches may be NULL only when they hold no page
-  if (!q || !page_table || !kv_lens || !sinks || ((!k_cache || !v_cache) && num_pages != 0))
-    return ATTN_SINK_ERR_INVALID_ARG;
-  if (num_splits < 1) return ATTN_SINK_ERR_INVALID_ARG;
-  if (num_splits == 1 && !out) return ATTN_SINK_ERR_INVALID_ARG;
-  if (num_splits > 1 && (!partial_m || !partial_d || !partial_o)) return ATTN_SINK_ERR_INVALID_ARG;
-  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
-      !aligned(page_table, 4) || !aligned(kv_lens, 4) || !aligned(sinks, 4) ||
-      (out && !aligned(out, 16)) || (partial_m && !aligned(partial_m, 4)) ||
-      (partial_d && !aligned(partial_d, 4)) || (partial_o && !aligned(partial_o, 16)))
-    return ATTN_SINK_ERR_INVALID_ARG;
-  if (batch < 0 || max_pages_per_seq < 1 || num_pages < 0 || num_kv_heads < 1 ||
-      group_size < 1 || head_dim < 1 || page_size < 1 ||
-      (dtype != ATTN_SINK_F32 && dtype != ATTN_SINK_BF16) || !finite_positive(sm_scale))
-    return ATTN_SINK_ERR_INVALID_ARG;
-  if (head_dim != kHeadDim || page_size != kPage || group_size > 16)
-    return ATTN_SINK_ERR_UNSUPPORTED;
-  if (batch > 65535 || num_kv_heads > 65535 ||
-      (int64_t)max_pages_per_seq * kPage > INT32_MAX ||
-      (int64_t)num_splits * max_pages_per_seq > INT32_MAX)
-    return ATTN_SINK_ERR_UNSUPPORTED;
-  if (batch == 0) return ATTN_SINK_OK;
-  const dim3 grid(num_splits, num_kv_heads, batch);
-  const float qk = sm_scale * kLog2e;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (dtype == ATTN_SINK_BF16)
-    hipLaunchKernelGGL((decode_kernel<DT_BF16, kDecodeWaves, kDecodeUnroll>), grid,
-                       dim3(64 * kDecodeWaves), 0, s, (const char*)q, (const char*)k_cache,
-                       (const char*)v_cache, page_table, kv_lens, sinks, max_pages_per_seq,
-                       num_pages, num_kv_heads, group_size, qk, num_splits, partial_m,
-                       partial_d, partial_o, (char*)out);
-  else
-    hipLaunchKernelGGL((decode_kernel<DT_F32, kDecodeWaves, kDecodeUnroll>), grid,
-                       dim3(64 * kDecodeWaves), 0, s, (const char*)q, (const char*)k_cache,
-                       (const char*)v_cache, page_table, kv_lens, sinks, max_pages_per_seq,
-                       num_pages, num_kv_heads, group_size, qk, num_splits, partial_m,
-                       partial_d, partial_o, (char*)out);
-  return launch_status();
+  return decode_paged_impl(q, k_cache, v_cache, page_table, kv_lens, sinks, batch,
+                           max_pages_per_seq, num_pages, num_kv_heads, group_size, head_dim,
+                           page_size, sm_scale, dtype, num_splits, partial_m, partial_d,
+                           partial_o, out, stream);
 }
 
 int attn_sink_merge(const float* partial_m, const float* partial_d, const float* partial_o,
                     int batch, int num_q_heads, int num_splits, int head_dim, int out_dtype,
                     void* out, void* stream) {
-  if (!partial_m || !partial_d || !partial_o || !out) return ATTN_SINK_ERR_INVALID_ARG;
-  if (!aligned(partial_m, 4) || !aligned(partial_d, 4) || !aligned(partial_o, 16) ||
-      !aligned(out, 16))
-    return ATTN_SINK_ERR_INVALID_ARG;
-  if (batch < 0 || num_q_heads < 1 || num_splits < 1 || head_dim < 1 ||
-      (out_dtype != ATTN_SINK_F32 && out_dtype != ATTN_SINK_BF16))
-    return ATTN_SINK_ERR_INVALID_ARG;
-  if (head_dim != kHeadDim) return ATTN_SINK_ERR_UNSUPPORTED;
-  const int64_t rows = (int64_t)batch * num_q_heads;
-  if (rows > INT32_MAX - 16) return ATTN_SINK_ERR_UNSUPPORTED;
-  if (rows == 0) return ATTN_SINK_OK;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const bool bf = out_dtype == ATTN_SINK_BF16;
-  // chunk lanes per row: up to 16, fewer when there are fewer splits
-  const int cl = num_splits >= 16 ? 16 : num_splits >= 8 ? 8 : num_splits >= 4 ? 4 : 2;
-  const int rpb = 256 / (16 * cl);
-  const dim3 grid((unsigned)((rows + rpb - 1) / rpb));
-#define ATTN_SINK_MERGE(CLV)                                                                  \
-  hipLaunchKernelGGL((bf ? merge_kernel<DT_BF16, CLV> : merge_kernel<DT_F32, CLV>), grid,      \
-                     dim3(256), 0, s, partial_m, partial_d, partial_o, (int)rows, num_splits,  \
-                     (char*)out)
-  switch (cl) {
-    case 16: ATTN_SINK_MERGE(16); break;
-    case 8: ATTN_SINK_MERGE(8); break;
-    case 4: ATTN_SINK_MERGE(4); break;
-    default: ATTN_SINK_MERGE(2); break;
-  }
-#undef ATTN_SINK_MERGE
-  return launch_status();
+  return merge_impl(partial_m, partial_d, partial_o, batch, num_q_heads, num_splits, head_dim,
+                    out_dtype, out, stream);
 }
 
 }  // extern "C"

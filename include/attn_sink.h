@@ -141,9 +141,8 @@ int attn_sink_prefill_partials(const void *q, const void *k, const void *v,
  *              partial_o [total_q, Hkv*G, S, D] as attn_sink_prefill_partials
  *              does; out is not touched and may be NULL.
  * q and out may be NULL when total_q == 0; the caches when num_pages == 0.
- * Each cache must be below 4 GiB (ATTN_SINK_ERR_UNSUPPORTED otherwise: its
- * pages are addressed with 32-bit buffer offsets); attn_sink_decode_paged
- * has no such limit.
+ * Caches of any size are accepted: below 4 GiB pages are read at 32-bit
+ * offsets from the cache base, from 4 GiB on through 64-bit page bases.
  */
 int attn_sink_prefill_paged(const void *q, const void *k_cache,
                             const void *v_cache, const int32_t *page_table,

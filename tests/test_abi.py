@@ -145,7 +145,8 @@ def test_prefill_partials_validation(L, kw, code):
     (dict(maxp=0), INVALID), (dict(npages=-1), INVALID), (dict(causal=-1), INVALID),
     (dict(dtype=2), INVALID), (dict(scale=0.0), INVALID),
     (dict(dim=32), UNSUPPORTED), (dict(page=8), UNSUPPORTED), (dict(group=80), UNSUPPORTED),
-    (dict(maxp=1 << 27), UNSUPPORTED), (dict(npages=1 << 20, hkv=8), UNSUPPORTED),
+    (dict(maxp=1 << 27), UNSUPPORTED),
+    (dict(npages=1 << 20, hkv=8, batch=0), OK),       # a 16 GiB cache is accepted
     (dict(kc=None, vc=None, npages=0, batch=0), OK), (dict(batch=0), OK),
     (dict(tq=0, q=None, out=None), OK),
     (dict(batch=0, splits=3, pm=A, pd=A, po=A, out=None), OK)])

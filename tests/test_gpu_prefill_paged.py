@@ -263,3 +263,38 @@ def test_chunked_prefill_workload_full(lib):
     assert_close(merged.cpu(), ref, torch.bfloat16, "chunked prefill split %d" % S)
     check_partials(got, oracle_paged(d, True, S), torch.bfloat16, d["sinks"][None, :],
                    "chunked prefill partials")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("splits", [1, 3])
+def test_paged_prefill_pages_past_4gib(lib, dtype, splits):
+    """Caches of 4 GiB or more (an engine-sized cache) are read through
+    64-bit page bases: with the same logical pages moved past the 4 GiB mark
+    of a 5 GiB cache, the result is bit for bit that of the compact cache,
+    and matches the oracle."""
+    d = paged_case([40, 130, 1], [300, 130, 77], 8, 2, dtype, seed=91)
+    small = run_paged(lib, d, True, splits)
+    dd = _dev(d)
+    kc, vc, pt = dd["k_cache"], dd["v_cache"], dd["page_table"]
+    block = kc[0].numel() * kc.element_size()
+    nbig = -(-(5 << 30) // block)
+    big = dict(dd)
+    big["k_cache"] = torch.empty((nbig,) + tuple(kc.shape[1:]), dtype=kc.dtype, device=DEV)
+    big["v_cache"] = torch.empty((nbig,) + tuple(vc.shape[1:]), dtype=vc.dtype, device=DEV)
+    n = kc.shape[0]
+    new_ids = nbig - 1 - torch.arange(n, device=DEV)
+    big["k_cache"][new_ids] = kc
+    big["v_cache"][new_ids] = vc
+    valid = (pt >= 0) & (pt < n)
+    big["page_table"] = torch.where(valid, nbig - 1 - pt, pt).to(torch.int32)
+    assert int(big["page_table"][valid].min()) * block >= (4 << 30)
+    got = run_paged(lib, big, True, splits)
+    del big
+    if splits == 1:
+        assert torch.equal(got.view(torch.int16) if dtype == torch.bfloat16 else got.view(torch.int32),
+                           small.view(torch.int16) if dtype == torch.bfloat16 else small.view(torch.int32))
+        assert_close(got, oracle_paged(d), dtype, "paged prefill, 5 GiB cache")
+    else:
+        for a, b in zip(got, small):
+            assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+        check_partials(got, oracle_paged(d, True, splits), dtype, d["sinks"], "5 GiB cache")
