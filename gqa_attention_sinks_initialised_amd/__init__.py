@@ -28,7 +28,8 @@ PAGE_SIZE = 16
 _lib = None
 
 SYMBOLS = ("attn_sink_prefill", "attn_sink_prefill_partials", "attn_sink_prefill_paged",
-           "attn_sink_decode_paged", "attn_sink_merge", "attn_sink_status_string")
+           "attn_sink_decode_paged", "attn_sink_merge", "attn_sink_decode_paged_static",
+           "attn_sink_status_string")
 
 
 class AttnSinkError(RuntimeError):
@@ -53,8 +54,11 @@ def load_library(path: str = LIB_PATH):
     lib.attn_sink_prefill_paged.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I,
                                             F, I, I, I, P, P, P, P, P]
     lib.attn_sink_merge.argtypes = [P, P, P, I, I, I, I, I, P, P]
+    lib.attn_sink_decode_paged_static.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, F, I,
+                                                  I, P, P]
     for f in (lib.attn_sink_prefill, lib.attn_sink_prefill_partials,
-              lib.attn_sink_prefill_paged, lib.attn_sink_decode_paged, lib.attn_sink_merge):
+              lib.attn_sink_prefill_paged, lib.attn_sink_decode_paged, lib.attn_sink_merge,
+              lib.attn_sink_decode_paged_static):
         f.restype = ctypes.c_int
     lib.attn_sink_status_string.argtypes = [I]
     lib.attn_sink_status_string.restype = ctypes.c_char_p
@@ -293,6 +297,41 @@ def attn_sink_merge(partial_m, partial_d, partial_o, out=None, out_dtype=None, s
         _ptr(partial_m), _ptr(partial_d), _ptr(partial_o), batch, hq, S, dim,
         _dtype_code(out), _ptr(out), _stream(stream))
     _check(rc, "attn_sink_merge")
+    return out
+
+
+def attn_sink_decode_paged_static(q, k_cache, v_cache, page_table, kv_lens, sinks,
+                                  group_size: int, sm_scale: float | None = None,
+                                  num_splits: int = 1, out=None, stream=None):
+    """Split paged decode + merge in one library call that allocates nothing:
+    the partial states live in the library's 16 MiB static device array.
+    Arguments as attn_sink_decode_paged; returns out [B, Hkv*G, 64].  Calls
+    that overlap on one GPU share that array and race."""
+    import torch
+    _dev(q, k_cache, v_cache, page_table, kv_lens, sinks, out)
+    dt = _dtype_code(q)
+    _need(k_cache.dtype == q.dtype and v_cache.dtype == q.dtype, "dtype mismatch")
+    _need(page_table.dtype == torch.int32 and kv_lens.dtype == torch.int32,
+          "page_table / kv_lens must be int32")
+    _need(k_cache.dim() == 4 and v_cache.dim() == 4, "caches must be 4-d")
+    num_pages, hkv, page, dim = k_cache.shape
+    _need(v_cache.shape == (num_pages, hkv, dim, page), "v_cache must be [pages, Hkv, D, P]")
+    _need(q.dim() == 3 and q.shape[2] == dim, "q must be [B, Hkv*G, D] with the caches' D")
+    batch, hq = q.shape[0], q.shape[1]
+    _need(hq == hkv * group_size, "q heads != kv heads * group_size")
+    _need(page_table.dim() == 2 and page_table.shape[0] == batch, "bad page_table")
+    _need(kv_lens.numel() == batch, "bad kv_lens")
+    _need(sinks.dtype == torch.float32 and sinks.numel() == hq, "bad sinks")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(dim)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out.shape == q.shape and out.dtype == q.dtype, "bad out tensor")
+    rc = load_library().attn_sink_decode_paged_static(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table), _ptr(kv_lens), _ptr(sinks),
+        batch, page_table.shape[1], num_pages, hkv, int(group_size), dim, page,
+        float(sm_scale), dt, int(num_splits), _ptr(out), _stream(stream))
+    _check(rc, "attn_sink_decode_paged_static")
     return out
 
 

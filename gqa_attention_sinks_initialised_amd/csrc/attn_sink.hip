@@ -38,10 +38,16 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 
 #include "attn_sink.h"
+
+// Device memory of attn_sink_decode_paged_static (see scratch_for below):
+// the split partial states of one call, at most kScratchBytes.
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
 
 namespace {
 
@@ -1752,6 +1758,39 @@ int merge_impl(const float* partial_m, const float* partial_d, const float* part
   return launch_status();
 }
 
+// ------------------------------------------------- static scratch (no-alloc)
+//
+// attn_sink_decode_paged_static keeps its split partial states in this
+// file-scope device array instead of caller- or library-allocated memory.
+// Each GPU the library runs on holds its own copy until the process ends.
+// In host code the array's name is only a host-side stand-in: its device
+// address is resolved once per device with hipGetSymbolAddress (with that
+// device current) and only that address is handed to kernels.
+
+std::mutex g_scratch_mu;
+constexpr int kMaxDevices = 64;
+char* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the scratch array on the device `stream` belongs to.
+int scratch_for(hipStream_t stream, char** out) {
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return ATTN_SINK_ERR_LAUNCH;
+  int dev = cur;
+  if (stream && hipStreamGetDevice(stream, &dev) != hipSuccess) return ATTN_SINK_ERR_INVALID_ARG;
+  if (dev < 0 || dev >= kMaxDevices) return ATTN_SINK_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return ATTN_SINK_ERR_LAUNCH;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur && hipSetDevice(cur) != hipSuccess) return ATTN_SINK_ERR_LAUNCH;
+    if (e != hipSuccess || !p) return ATTN_SINK_ERR_LAUNCH;
+    g_scratch_ptr[dev] = static_cast<char*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return ATTN_SINK_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1762,6 +1801,8 @@ const char* attn_sink_status_string(int status) {
     case ATTN_SINK_ERR_INVALID_ARG: return "invalid argument";
     case ATTN_SINK_ERR_UNSUPPORTED: return "unsupported configuration";
     case ATTN_SINK_ERR_LAUNCH: return "kernel launch failed";
+    case ATTN_SINK_ERR_TOO_LARGE:
+      return "split partial states exceed the 16 MiB static scratch buffer";
     default: return "unknown status";
   }
 }
@@ -1871,6 +1912,43 @@ int attn_sink_merge(const float* partial_m, const float* partial_d, const float*
                     void* out, void* stream) {
   return merge_impl(partial_m, partial_d, partial_o, batch, num_q_heads, num_splits, head_dim,
                     out_dtype, out, stream);
+}
+
+int attn_sink_decode_paged_static(const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* page_table, const int32_t* kv_lens,
+                                  const float* sinks, int batch, int max_pages_per_seq,
+                                  int num_pages, int num_kv_heads, int group_size, int head_dim,
+                                  int page_size, float sm_scale, int dtype, int num_splits,
+                                  void* out, void* stream) {
+  const int rc0 = check_decode_args(q, k_cache, v_cache, page_table, kv_lens, sinks, batch,
+                                    max_pages_per_seq, num_pages, num_kv_heads, group_size,
+                                    head_dim, page_size, sm_scale, dtype, num_splits);
+  if (rc0 != ATTN_SINK_OK) return rc0;
+  if (!out || !aligned(out, 16)) return ATTN_SINK_ERR_INVALID_ARG;
+  if (num_splits == 1)
+    return decode_paged_impl(q, k_cache, v_cache, page_table, kv_lens, sinks, batch,
+                             max_pages_per_seq, num_pages, num_kv_heads, group_size, head_dim,
+                             page_size, sm_scale, dtype, 1, nullptr, nullptr, nullptr, out,
+                             stream);
+  // partial states of (batch x Hq) rows x S chunks: m, d, then o, each
+  // region 256-byte aligned inside the scratch array
+  const int64_t states = (int64_t)batch * num_kv_heads * group_size * num_splits;
+  const int64_t md_bytes = (states * 4 + 255) / 256 * 256;
+  if (2 * md_bytes + states * kHeadDim * 4 > (int64_t)kScratchBytes) return ATTN_SINK_ERR_TOO_LARGE;
+  if (batch == 0) return ATTN_SINK_OK;
+  char* base = nullptr;
+  const int rc = scratch_for(reinterpret_cast<hipStream_t>(stream), &base);
+  if (rc != ATTN_SINK_OK) return rc;
+  float* pm = reinterpret_cast<float*>(base);
+  float* pd = reinterpret_cast<float*>(base + md_bytes);
+  float* po = reinterpret_cast<float*>(base + 2 * md_bytes);
+  const int rc2 = decode_paged_impl(q, k_cache, v_cache, page_table, kv_lens, sinks, batch,
+                                    max_pages_per_seq, num_pages, num_kv_heads, group_size,
+                                    head_dim, page_size, sm_scale, dtype, num_splits, pm, pd, po,
+                                    nullptr, stream);
+  if (rc2 != ATTN_SINK_OK) return rc2;
+  return merge_impl(pm, pd, po, batch, num_kv_heads * group_size, num_splits, head_dim, dtype,
+                    out, stream);
 }
 
 }  // extern "C"

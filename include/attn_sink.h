@@ -53,7 +53,8 @@ typedef enum {
     ATTN_SINK_OK = 0,
     ATTN_SINK_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size or flag */
     ATTN_SINK_ERR_UNSUPPORTED = 2, /* valid but not built: head_dim, page size, group */
-    ATTN_SINK_ERR_LAUNCH = 3       /* the HIP runtime refused the launch */
+    ATTN_SINK_ERR_LAUNCH = 3,      /* the HIP runtime refused the launch */
+    ATTN_SINK_ERR_TOO_LARGE = 4    /* exceeds the static scratch buffer (no-alloc call) */
 } attn_sink_status;
 
 typedef enum { ATTN_SINK_F32 = 0, ATTN_SINK_BF16 = 1 } attn_sink_dtype;
@@ -206,6 +207,38 @@ int attn_sink_merge(const float *partial_m, const float *partial_d,
                     const float *partial_o, int batch, int num_q_heads,
                     int num_splits, int head_dim, int out_dtype, void *out,
                     void *stream);
+
+/*
+ * Split paged decode and merge in one call that allocates nothing: for
+ * callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ *   Arguments as in attn_sink_decode_paged; out [batch, Hkv*G, D] dtype is
+ *   always written.  With num_splits == 1 this is attn_sink_decode_paged.
+ *   With num_splits > 1 the partial states go to a file-scope device array
+ *   of 16 MiB inside the library instead of caller buffers, and the merge
+ *   runs on `stream` right after the decode; the result is bit for bit
+ *   that of attn_sink_decode_paged + attn_sink_merge.
+ *   Limit: 4 * batch * Hkv*G * num_splits * (D + 2) bytes (plus alignment)
+ *   must fit in 16 MiB, else ATTN_SINK_ERR_TOO_LARGE and nothing is
+ *   enqueued.
+ *   Each GPU holds one copy of the array for the life of the process, and
+ *   every call on that GPU uses it: calls that may overlap on one GPU (on
+ *   different streams, or from different threads) race and must be
+ *   serialised by the caller.  Nothing in the array needs clearing: every
+ *   call writes every partial state it later reads.  The first call on a
+ *   device resolves the array's device address (hipGetSymbolAddress); no
+ *   call allocates, frees or synchronises.
+ */
+int attn_sink_decode_paged_static(const void *q, const void *k_cache,
+                                  const void *v_cache,
+                                  const int32_t *page_table,
+                                  const int32_t *kv_lens, const float *sinks,
+                                  int batch, int max_pages_per_seq,
+                                  int num_pages, int num_kv_heads,
+                                  int group_size, int head_dim, int page_size,
+                                  float sm_scale, int dtype, int num_splits,
+                                  void *out, void *stream);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char *attn_sink_status_string(int status);

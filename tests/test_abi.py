@@ -34,7 +34,8 @@ def L():
 def test_header_declares_the_entry_points():
     names = _declared_functions()
     for n in ("attn_sink_prefill", "attn_sink_prefill_partials", "attn_sink_prefill_paged",
-              "attn_sink_decode_paged", "attn_sink_merge", "attn_sink_status_string"):
+              "attn_sink_decode_paged", "attn_sink_merge", "attn_sink_decode_paged_static",
+              "attn_sink_status_string"):
         assert n in names
 
 
@@ -49,6 +50,7 @@ def test_status_strings(L):
     assert m.status_string(INVALID) == "invalid argument"
     assert m.status_string(UNSUPPORTED) == "unsupported configuration"
     assert m.status_string(LAUNCH) == "kernel launch failed"
+    assert "static scratch" in m.status_string(4)
     assert m.status_string(99) == "unknown status"
 
 
@@ -169,3 +171,26 @@ def test_binding_refuses_cpu_tensors(L):
     cu = torch.tensor([0, 4], dtype=torch.int32)
     with pytest.raises(ValueError):
         m.attn_sink_prefill(q, k, k, torch.zeros(2), cu, cu, 4, 2)
+
+
+TOO_LARGE = 4
+
+
+def _decode_static(L, **kw):
+    args = dict(q=A, kc=A, vc=A, pt=A, lens=A, sinks=A, batch=1, maxp=4, npages=4, hkv=1,
+                group=1, dim=64, page=16, scale=0.125, dtype=1, splits=2, out=A, stream=None)
+    args.update(kw)
+    return L.attn_sink_decode_paged_static(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INVALID), (dict(out=None), INVALID), (dict(out=MIS), INVALID),
+    (dict(splits=0), INVALID), (dict(kc=MIS), INVALID), (dict(dtype=5), INVALID),
+    (dict(dim=32), UNSUPPORTED), (dict(group=17), UNSUPPORTED),
+    # 64 x 64 rows x 128 chunks of (64 + 2) floats: 138 MB > 16 MiB
+    (dict(batch=64, hkv=8, group=8, splits=128), TOO_LARGE),
+    (dict(batch=0, splits=3), OK), (dict(batch=0, splits=1), OK)])
+def test_decode_static_validation(L, kw, code):
+    """The no-alloc entry point rejects bad arguments, and work whose split
+    states would not fit its static scratch array, before anything runs."""
+    assert _decode_static(L, **kw) == code
