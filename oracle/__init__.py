@@ -25,7 +25,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# ORACLE_LIBRARY points the tests at another build of oracle.c (the mutation
+# test builds copies with planted mistakes and checks that the pins fail).
+_LIB_PATH = os.environ.get("ORACLE_LIBRARY") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 F32, BF16, F64 = 0, 1, 2
