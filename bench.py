@@ -99,6 +99,22 @@ def profiled_clock():
     return rec.get("clock_ghz")
 
 
+def profiled_power():
+    """Socket power per kernel and the vendor bf16 GEMM reference under the same power cap,
+    from `bench.py --power` (profiles/power.json), while the kernel source hash matches."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "power.json")
+    src = os.path.join(ROOT, "gqa_attention_sinks_initialised_amd", "csrc", "attn_sink.hip")
+    try:
+        rec = json.load(open(path))
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != sha:
+        return None
+    return rec
+
+
 def cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -120,6 +136,9 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (reference for the "
                          "HBM byte counters)")
+    ap.add_argument("--power", action="store_true",
+                    help="only measure socket power and shader clocks (amd-smi) while each "
+                         "main kernel runs back to back for a few seconds")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only; run with --gpus 1 "
@@ -142,6 +161,9 @@ def main():
     attn.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.power:
+        power_profile(attn, workloads, torch, dev)
+        return
 
     # ---- inputs (seeded, synthetic), resident in HBM before timing
     c2 = workloads.workload(2, device=dev)
@@ -295,6 +317,9 @@ def main():
     traffic = counted_traffic() or {}
     clock = profiled_clock() or {}
     clk2 = clock.get("prefill")
+    power = profiled_power() or {}
+    pk = power.get("kernels", {})
+    gemm_ref = pk.get("library_gemm_bf16_8192", {}).get("rate")
     result = {
         "metric": "prefill attention TFLOP/s (bf16) + decode KV-read HBM GB/s, % of roofline",
         "value": round(tflops, 2),
@@ -321,7 +346,12 @@ def main():
                      **spread("prefill"),
                      "clock_ghz": clk2,
                      "frac_at_clock": (round(tflops / (PEAK_BF16_TFLOPS * clk2 / 2.4), 4)
-                                       if clk2 else None)},
+                                       if clk2 else None),
+                     "power_w": pk.get("prefill", {}).get("power_w"),
+                     "power_cap_w": power.get("power_cap_w"),
+                     "gemm_reference_tflops": gemm_ref,
+                     "frac_of_gemm_reference": (round(tflops / gemm_ref, 4)
+                                                if gemm_ref else None)},
         "decode": {"workload": c3["name"], "splits": s3,
                    "us_decode": round(t["decode"] * 1e3, 2),
                    "us_merge": round(t["decode_merge"] * 1e3, 2),
@@ -373,6 +403,107 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(c2, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def _smi_sample():
+    """Socket power (W) and the mean shader clock over the XCDs (MHz) from amd-smi,
+    or None when the tool gives nothing usable."""
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-p", "-c", "--json"], capture_output=True,
+                           text=True, timeout=15)
+        d = json.loads(r.stdout)
+    except (OSError, ValueError, subprocess.SubprocessError):
+        return None
+    gpu = (d.get("gpu_data") or [d])[0] if isinstance(d, dict) else d[0]
+    try:
+        watts = float(gpu["power"]["socket_power"]["value"])
+        clocks = [float(v["clk"]["value"]) for k, v in gpu["clock"].items()
+                  if k.startswith("gfx_") and isinstance(v, dict) and "clk" in v]
+    except (KeyError, TypeError, ValueError):
+        return None
+    return watts, (sum(clocks) / len(clocks) if clocks else None)
+
+
+def power_profile(attn, workloads, torch, dev, seconds=4.0):
+    """Each main kernel back to back for `seconds`; amd-smi is sampled from a thread
+    after the first second.  Prints one JSON line: per kernel the mean socket power,
+    shader clock, achieved rate and the dynamic energy per unit of work, beside the
+    idle power."""
+    import threading
+    c2 = workloads.workload(2, device=dev)
+    c5 = workloads.workload(5, device=dev)
+    c3 = workloads.workload(3, device=dev, cache_device=dev)
+    o2, o5 = torch.empty_like(c2["q"]), torch.empty_like(c5["q"])
+    mq5 = max(c5["lens_q"])
+    kernels = [
+        ("prefill", "TFLOP/s", prefill_flops(c2["lens_q"], c2["lens_kv"], 64, 64) / 1e12,
+         lambda: attn.attn_sink_prefill(c2["q"], c2["k"], c2["v"], c2["sinks"],
+                                        c2["cu_seqlens_q"], c2["cu_seqlens_kv"], 2048, 8,
+                                        c2["sm_scale"], True, out=o2)),
+        ("ragged_prefill", "TFLOP/s", prefill_flops(c5["lens_q"], c5["lens_kv"], 64, 64) / 1e12,
+         lambda: attn.attn_sink_prefill(c5["q"], c5["k"], c5["v"], c5["sinks"],
+                                        c5["cu_seqlens_q"], c5["cu_seqlens_kv"], mq5, 8,
+                                        c5["sm_scale"], True, out=o5)),
+        ("decode_paged_unsplit", "TB/s",
+         decode_bytes(c3["kv_lens"].tolist(), 64, 8, 64, 1)["decode"] / 1e12,
+         lambda: attn.attn_sink_decode_paged(c3["q"], c3["k_cache"], c3["v_cache"],
+                                             c3["page_table"], c3["kv_lens"], c3["sinks"], 8,
+                                             c3["sm_scale"], 1)),
+    ]
+    # reference: a plain bf16 matrix product from the vendor library (hipBLASLt through
+    # torch.mm on contiguous operands), the practical MFMA rate under the same power cap
+    ga = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
+    gb = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
+    gc = torch.empty(8192, 8192, device=dev, dtype=torch.bfloat16)
+    kernels.append(("library_gemm_bf16_8192", "TFLOP/s", 2.0 * 8192 ** 3 / 1e12,
+                    lambda: torch.mm(ga, gb, out=gc)))
+    torch.cuda.synchronize()
+    time.sleep(2.0)
+    idle = [x for x in (_smi_sample() for _ in range(3)) if x]
+    res = {"metric": "socket power and shader clock per kernel (back-to-back launches)",
+           "idle_w": round(sum(w for w, _ in idle) / len(idle), 1) if idle else None,
+           "power_cap_w": 1400.0, "kernels": {}}
+    for name, unit, work, fn in kernels:
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        samples, stop = [], threading.Event()
+        t_start = time.perf_counter()
+
+        def sampler():
+            while not stop.is_set():
+                if time.perf_counter() - t_start > 1.0:
+                    x = _smi_sample()
+                    if x:
+                        samples.append(x)
+                time.sleep(0.2)
+
+        th = threading.Thread(target=sampler)
+        th.start()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        n = 0
+        while time.perf_counter() - t_start < seconds:
+            fn()
+            n += 1
+        e1.record()
+        torch.cuda.synchronize()
+        stop.set()
+        th.join()
+        rate = work * n / (e0.elapsed_time(e1) * 1e-3)
+        rec = {"launches": n, "rate": round(rate, 2), "unit": unit, "samples": len(samples)}
+        if samples:
+            w = sum(x[0] for x in samples) / len(samples)
+            clk = [x[1] for x in samples if x[1]]
+            rec.update(power_w=round(w, 1),
+                       clock_mhz=round(sum(clk) / len(clk), 0) if clk else None)
+            if res["idle_w"] is not None:
+                per = "pJ/flop" if unit == "TFLOP/s" else "pJ/byte"
+                rec["dynamic_energy"] = round((w - res["idle_w"]) / rate, 3)
+                rec["dynamic_energy_unit"] = per
+        res["kernels"][name] = rec
+    print(json.dumps(res), flush=True)
 
 
 def cpu_baseline(c2, target_s):
