@@ -88,24 +88,37 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _stream(stream):
-    import torch
-    if stream is None:
-        stream = torch.cuda.current_stream()
-    return ctypes.c_void_p(stream.cuda_stream)
-
-
 def _need(cond, msg):
     if not cond:
         raise ValueError(msg)
 
 
 def _dev(*ts):
+    """Check that the tensors are contiguous and on one GPU; return it."""
+    dev = None
     for t in ts:
         if t is None:
             continue
         _need(t.is_cuda, "all tensors must be on the GPU")
         _need(t.is_contiguous(), "all tensors must be contiguous")
+        if dev is None:
+            dev = t.device
+        _need(t.device == dev, "all tensors must be on the same GPU")
+    return dev
+
+
+def _invoke(name, device, stream, *args):
+    """Call library entry point `name` with `args` and the stream, with the
+    tensors' GPU current (a null stream means that GPU's null stream).
+    Without a stream, the tensors' GPU's current torch stream is used."""
+    import torch
+    lib = load_library()
+    with torch.cuda.device(device):
+        if stream is None:
+            stream = torch.cuda.current_stream(device)
+        _need(stream.device == device, "the stream is on another GPU than the tensors")
+        rc = getattr(lib, name)(*args, ctypes.c_void_p(stream.cuda_stream))
+    _check(rc, name)
 
 
 def attn_sink_prefill(q, k, v, sinks, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int,
@@ -114,7 +127,7 @@ def attn_sink_prefill(q, k, v, sinks, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q:
     """Ragged prefill.  q [total_q, Hkv*G, 64], k/v [total_kv, Hkv, 64] (bf16 or
     fp32), sinks [Hkv*G] fp32, cu_seqlens_* [B+1] int32.  Returns out."""
     import torch
-    _dev(q, k, v, sinks, cu_seqlens_q, cu_seqlens_kv, out)
+    dev = _dev(q, k, v, sinks, cu_seqlens_q, cu_seqlens_kv, out)
     dt = _dtype_code(q)
     _need(k.dtype == q.dtype and v.dtype == q.dtype, "q, k, v dtypes differ")
     _need(sinks.dtype == torch.float32, "sinks must be float32")
@@ -132,11 +145,10 @@ def attn_sink_prefill(q, k, v, sinks, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q:
     if out is None:
         out = torch.empty_like(q)
     _need(out.shape == q.shape and out.dtype == q.dtype, "bad out tensor")
-    rc = load_library().attn_sink_prefill(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(sinks), _ptr(cu_seqlens_q), _ptr(cu_seqlens_kv),
-        batch, q.shape[0], k.shape[0], int(max_seqlen_q), hkv, int(group_size), q.shape[2],
-        float(sm_scale), int(bool(causal)), dt, _ptr(out), _stream(stream))
-    _check(rc, "attn_sink_prefill")
+    _invoke("attn_sink_prefill", dev, stream,
+            _ptr(q), _ptr(k), _ptr(v), _ptr(sinks), _ptr(cu_seqlens_q), _ptr(cu_seqlens_kv),
+            batch, q.shape[0], k.shape[0], int(max_seqlen_q), hkv, int(group_size), q.shape[2],
+            float(sm_scale), int(bool(causal)), dt, _ptr(out))
     return out
 
 
@@ -166,7 +178,7 @@ def attn_sink_prefill_partials(q, k, v, sinks, cu_seqlens_q, cu_seqlens_kv,
     shapes [total_q, Hq, S], [total_q, Hq, S], [total_q, Hq, S, 64] for
     attn_sink_merge (batch = total_q)."""
     import torch
-    _dev(q, k, v, sinks, cu_seqlens_q, cu_seqlens_kv, partial_m, partial_d, partial_o)
+    dev = _dev(q, k, v, sinks, cu_seqlens_q, cu_seqlens_kv, partial_m, partial_d, partial_o)
     dt = _dtype_code(q)
     _need(k.dtype == q.dtype and v.dtype == q.dtype, "q, k, v dtypes differ")
     _need(sinks.dtype == torch.float32, "sinks must be float32")
@@ -182,12 +194,10 @@ def attn_sink_prefill_partials(q, k, v, sinks, cu_seqlens_q, cu_seqlens_kv,
         sm_scale = 1.0 / math.sqrt(q.shape[2])
     S = int(num_splits)
     pm, pd, po = _partials(q, S, partial_m, partial_d, partial_o)
-    rc = load_library().attn_sink_prefill_partials(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(sinks), _ptr(cu_seqlens_q), _ptr(cu_seqlens_kv),
-        batch, q.shape[0], k.shape[0], int(max_seqlen_q), hkv, int(group_size), q.shape[2],
-        float(sm_scale), int(bool(causal)), dt, S, _ptr(pm), _ptr(pd), _ptr(po),
-        _stream(stream))
-    _check(rc, "attn_sink_prefill_partials")
+    _invoke("attn_sink_prefill_partials", dev, stream,
+            _ptr(q), _ptr(k), _ptr(v), _ptr(sinks), _ptr(cu_seqlens_q), _ptr(cu_seqlens_kv),
+            batch, q.shape[0], k.shape[0], int(max_seqlen_q), hkv, int(group_size), q.shape[2],
+            float(sm_scale), int(bool(causal)), dt, S, _ptr(pm), _ptr(pd), _ptr(po))
     return pm, pd, po
 
 
@@ -201,8 +211,8 @@ def attn_sink_prefill_paged(q, k_cache, v_cache, page_table, cu_seqlens_q, kv_le
     tokens' included).  num_splits == 1 returns out; num_splits > 1 returns
     (partial_m, partial_d, partial_o) for attn_sink_merge."""
     import torch
-    _dev(q, k_cache, v_cache, page_table, cu_seqlens_q, kv_lens, sinks, partial_m, partial_d,
-         partial_o, out)
+    dev = _dev(q, k_cache, v_cache, page_table, cu_seqlens_q, kv_lens, sinks, partial_m,
+               partial_d, partial_o, out)
     dt = _dtype_code(q)
     _need(k_cache.dtype == q.dtype and v_cache.dtype == q.dtype, "dtype mismatch")
     _need(page_table.dtype == torch.int32 and kv_lens.dtype == torch.int32 and
@@ -225,12 +235,11 @@ def attn_sink_prefill_paged(q, k_cache, v_cache, page_table, cu_seqlens_q, kv_le
         pm = pd = po = None
     else:
         pm, pd, po = _partials(q, S, partial_m, partial_d, partial_o)
-    rc = load_library().attn_sink_prefill_paged(
-        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table), _ptr(cu_seqlens_q),
-        _ptr(kv_lens), _ptr(sinks), batch, q.shape[0], int(max_seqlen_q), page_table.shape[1],
-        num_pages, hkv, int(group_size), dim, page, float(sm_scale), int(bool(causal)), dt, S,
-        _ptr(pm), _ptr(pd), _ptr(po), _ptr(out), _stream(stream))
-    _check(rc, "attn_sink_prefill_paged")
+    _invoke("attn_sink_prefill_paged", dev, stream,
+            _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table), _ptr(cu_seqlens_q),
+            _ptr(kv_lens), _ptr(sinks), batch, q.shape[0], int(max_seqlen_q),
+            page_table.shape[1], num_pages, hkv, int(group_size), dim, page, float(sm_scale),
+            int(bool(causal)), dt, S, _ptr(pm), _ptr(pd), _ptr(po), _ptr(out))
     return out if S == 1 else (pm, pd, po)
 
 
@@ -243,8 +252,8 @@ def attn_sink_decode_paged(q, k_cache, v_cache, page_table, kv_lens, sinks,
     kv_lens [B] int32.  num_splits == 1 returns out; num_splits > 1 fills and
     returns (partial_m, partial_d, partial_o) for attn_sink_merge."""
     import torch
-    _dev(q, k_cache, v_cache, page_table, kv_lens, sinks, partial_m, partial_d,
-         partial_o, out)
+    dev = _dev(q, k_cache, v_cache, page_table, kv_lens, sinks, partial_m, partial_d,
+               partial_o, out)
     dt = _dtype_code(q)
     _need(k_cache.dtype == q.dtype and v_cache.dtype == q.dtype, "dtype mismatch")
     _need(page_table.dtype == torch.int32 and kv_lens.dtype == torch.int32,
@@ -268,19 +277,18 @@ def attn_sink_decode_paged(q, k_cache, v_cache, page_table, kv_lens, sinks,
         _need(out.shape == q.shape and out.dtype == q.dtype, "bad out tensor")
     else:
         partial_m, partial_d, partial_o = _partials(q, S, partial_m, partial_d, partial_o)
-    rc = load_library().attn_sink_decode_paged(
-        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table), _ptr(kv_lens), _ptr(sinks),
-        batch, page_table.shape[1], num_pages, hkv, int(group_size), dim, page,
-        float(sm_scale), dt, S, _ptr(partial_m), _ptr(partial_d), _ptr(partial_o),
-        _ptr(out), _stream(stream))
-    _check(rc, "attn_sink_decode_paged")
+    _invoke("attn_sink_decode_paged", dev, stream,
+            _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table), _ptr(kv_lens),
+            _ptr(sinks), batch, page_table.shape[1], num_pages, hkv, int(group_size), dim,
+            page, float(sm_scale), dt, S, _ptr(partial_m), _ptr(partial_d), _ptr(partial_o),
+            _ptr(out))
     return out if S == 1 else (partial_m, partial_d, partial_o)
 
 
 def attn_sink_merge(partial_m, partial_d, partial_o, out=None, out_dtype=None, stream=None):
     """Merge split states: m, d [B, Hq, S], o [B, Hq, S, 64] fp32 -> [B, Hq, 64]."""
     import torch
-    _dev(partial_m, partial_d, partial_o, out)
+    dev = _dev(partial_m, partial_d, partial_o, out)
     _need(partial_m.dim() == 3 and partial_o.dim() == 4, "bad partial shapes")
     batch, hq, S = partial_m.shape
     dim = partial_o.shape[-1]
@@ -293,10 +301,9 @@ def attn_sink_merge(partial_m, partial_d, partial_o, out=None, out_dtype=None, s
                           dtype=out_dtype or torch.bfloat16)
     _need(out.shape == (batch, hq, dim), "out must be [B, Hq, D]")
     _need(out_dtype is None or out.dtype == out_dtype, "out dtype differs from out_dtype")
-    rc = load_library().attn_sink_merge(
-        _ptr(partial_m), _ptr(partial_d), _ptr(partial_o), batch, hq, S, dim,
-        _dtype_code(out), _ptr(out), _stream(stream))
-    _check(rc, "attn_sink_merge")
+    _invoke("attn_sink_merge", dev, stream,
+            _ptr(partial_m), _ptr(partial_d), _ptr(partial_o), batch, hq, S, dim,
+            _dtype_code(out), _ptr(out))
     return out
 
 
@@ -308,7 +315,7 @@ def attn_sink_decode_paged_static(q, k_cache, v_cache, page_table, kv_lens, sink
     Arguments as attn_sink_decode_paged; returns out [B, Hkv*G, 64].  Calls
     that overlap on one GPU share that array and race."""
     import torch
-    _dev(q, k_cache, v_cache, page_table, kv_lens, sinks, out)
+    dev = _dev(q, k_cache, v_cache, page_table, kv_lens, sinks, out)
     dt = _dtype_code(q)
     _need(k_cache.dtype == q.dtype and v_cache.dtype == q.dtype, "dtype mismatch")
     _need(page_table.dtype == torch.int32 and kv_lens.dtype == torch.int32,
@@ -327,11 +334,10 @@ def attn_sink_decode_paged_static(q, k_cache, v_cache, page_table, kv_lens, sink
     if out is None:
         out = torch.empty_like(q)
     _need(out.shape == q.shape and out.dtype == q.dtype, "bad out tensor")
-    rc = load_library().attn_sink_decode_paged_static(
-        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table), _ptr(kv_lens), _ptr(sinks),
-        batch, page_table.shape[1], num_pages, hkv, int(group_size), dim, page,
-        float(sm_scale), dt, int(num_splits), _ptr(out), _stream(stream))
-    _check(rc, "attn_sink_decode_paged_static")
+    _invoke("attn_sink_decode_paged_static", dev, stream,
+            _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table), _ptr(kv_lens),
+            _ptr(sinks), batch, page_table.shape[1], num_pages, hkv, int(group_size), dim,
+            page, float(sm_scale), dt, int(num_splits), _ptr(out))
     return out
 
 

@@ -194,3 +194,25 @@ def test_decode_static_validation(L, kw, code):
     """The no-alloc entry point rejects bad arguments, and work whose split
     states would not fit its static scratch array, before anything runs."""
     assert _decode_static(L, **kw) == code
+
+
+class _FakeGpuTensor:
+    """Stands in for a contiguous GPU tensor: _dev reads only these fields."""
+
+    def __init__(self, device):
+        self.device, self.is_cuda = device, True
+
+    def is_contiguous(self):
+        return True
+
+
+def test_binding_requires_one_gpu_for_all_tensors():
+    """The library launches on the stream's GPU with the tensors' addresses,
+    so the binding refuses tensors spread over two GPUs before any call."""
+    import torch
+    a, b = torch.device("cuda:0"), torch.device("cuda:1")
+    assert m._dev(_FakeGpuTensor(a), None, _FakeGpuTensor(a)) == a
+    with pytest.raises(ValueError, match="same GPU"):
+        m._dev(_FakeGpuTensor(a), _FakeGpuTensor(b))
+    with pytest.raises(ValueError, match="on the GPU"):
+        m._dev(torch.zeros(2))

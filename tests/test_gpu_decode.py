@@ -319,3 +319,21 @@ def test_binding_rejects_misshaped_buffers(lib):
     with pytest.raises(ValueError):
         lib.attn_sink_merge(pm, pd, po, out=torch.empty((2, 8, 64), **f32),
                             out_dtype=torch.bfloat16)
+
+
+def test_explicit_side_stream_gives_the_default_stream_result(lib):
+    """Calls take an explicit stream; the result on a side stream is the
+    default stream's, bit for bit (the decode kernels are deterministic)."""
+    d = _to_dev(workloads.decode_inputs([300, 17, 1000], hq=16, hkv=2, dtype=torch.bfloat16,
+                                        seed=3))
+    args = (d["q"], d["k_cache"], d["v_cache"], d["page_table"], d["kv_lens"], d["sinks"],
+            d["group"], d["sm_scale"])
+    ref = lib.attn_sink_merge(*lib.attn_sink_decode_paged(*args, 3), out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        parts = lib.attn_sink_decode_paged(*args, 3, stream=side)
+        got = lib.attn_sink_merge(*parts, out_dtype=torch.bfloat16, stream=side)
+    side.synchronize()
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
