@@ -3,6 +3,8 @@
 One step = one pass over every stage of the path on its synthetic workload:
   prefill  causal prefill, bf16, B=4 x 2048, Hq=64, Hkv=8, D=64      (MFMA-bound)
   decode   paged decode, bf16, B=64, kv_len U[512,8192], + merge     (HBM-bound)
+  single   the same decode in one launch: unsplit, 16 waves per workgroup split
+           each sequence's pages and merge in LDS (no partial states, no merge)
   split    split-KV decode, bf16, B=4, kv_len 131072, 64 splits, + merge (HBM-bound)
   paged    the prefill workload with keys and values in a paged cache
   chunked  chunked prefill: B=1, 512 new tokens on a 32768-key paged cache,
@@ -181,6 +183,7 @@ def main():
 
     p3, p4 = mk_partials(64, s3), mk_partials(4, s4)
     o3 = torch.empty((64, hq, 64), device=dev, dtype=torch.bfloat16)
+    o3s = torch.empty((64, hq, 64), device=dev, dtype=torch.bfloat16)
     o4 = torch.empty((4, hq, 64), device=dev, dtype=torch.bfloat16)
     # Reading (not writing) 1 GiB evicts the 256 MB memory-side cache without
     # leaving dirty lines whose write-back would land inside the next kernel.
@@ -195,6 +198,10 @@ def main():
                                     c["kv_lens"], c["sinks"], 8, c["sm_scale"], s,
                                     partial_m=parts[0], partial_d=parts[1],
                                     partial_o=parts[2])
+
+    def run_decode_single():
+        attn.attn_sink_decode_paged(c3["q"], c3["k_cache"], c3["v_cache"], c3["page_table"],
+                                    c3["kv_lens"], c3["sinks"], 8, c3["sm_scale"], 1, out=o3s)
 
     # NEXT-row workloads: the prefill workload with its keys in a paged cache,
     # and chunked prefill (few query tiles, long paged cache) unsplit and split.
@@ -239,6 +246,8 @@ def main():
         ("_flush", flush.sum, False),
         ("decode", lambda: run_decode(c3, s3, p3), False),
         ("decode_merge", lambda: attn.attn_sink_merge(*p3, out=o3), True),
+        ("_flush", flush.sum, False),
+        ("decode_single", run_decode_single, False),
         ("_flush", flush.sum, False),
         ("split", lambda: run_decode(c4, s4, p4), False),
         ("split_merge", lambda: attn.attn_sink_merge(*p4, out=o4), True),
@@ -286,7 +295,7 @@ def main():
     # for the per-kernel split of each decode + merge bracket.
     tb, sb, wall = timed(args.steps, False)
     t, _, _ = timed(min(args.steps, 10), True)
-    for name in ("prefill", "paged_prefill", "chunked", "ragged_prefill"):
+    for name in ("prefill", "paged_prefill", "chunked", "ragged_prefill", "decode_single"):
         t[name] = tb[name]
 
     def spread(name):
@@ -304,6 +313,8 @@ def main():
     gbs4 = b4["total"] / (tb["split"] * 1e-3) / 1e9
     gbs3_k = b3["decode"] / (t["decode"] * 1e-3) / 1e9
     gbs4_k = b4["decode"] / (t["split"] * 1e-3) / 1e9
+    b3s = decode_bytes(c3["kv_lens"].tolist(), hq, 8, 64, 1)
+    gbs3s = b3s["total"] / (t["decode_single"] * 1e-3) / 1e9
 
     fl2p = fl2
     fl6 = prefill_flops(c6["lens_q"], c6["lens_kv"], hq, 64)
@@ -363,6 +374,14 @@ def main():
                    "decode_kernel_GB/s": round(gbs3_k, 1),
                    "decode_kernel_frac": round(gbs3_k / PEAK_HBM_GBS, 4),
                    "traffic": traffic.get("decode_paged")},
+        "decode_single_launch": {"workload": c3["name"] + ", one launch: unsplit, 16 waves "
+                                                 "per workgroup merged in LDS",
+                                 "splits": 1, "us": round(t["decode_single"] * 1e3, 2),
+                                 **spread("decode_single"),
+                                 "clock_ghz": clock.get("decode_single"),
+                                 "bytes": b3s["total"], "GB/s": round(gbs3s, 1),
+                                 "frac": round(gbs3s / PEAK_HBM_GBS, 4),
+                                 "traffic": traffic.get("decode_single")},
         "split_decode": {"workload": c4["name"], "splits": s4,
                          "us_decode": round(t["split"] * 1e3, 2),
                          "us_merge": round(t["split_merge"] * 1e3, 2),

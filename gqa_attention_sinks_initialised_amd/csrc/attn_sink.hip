@@ -20,7 +20,11 @@
 //                   (stored dim-major, so that the P.V contraction over
 //                   tokens reads contiguous memory) straight into MFMA
 //                   operands, K as whole 128-byte rows re-dealt into the
-//                   operand layout through 2 KB of LDS per wave.
+//                   operand layout through 2 KB of LDS per wave.  The waves
+//                   of a workgroup take interleaved pages of its chunk and
+//                   merge their states in LDS; unsplit decode runs 16 waves
+//                   per workgroup, so a sequence's whole key range is split
+//                   and merged inside one launch without partial states.
 //   merge_kernel    split-KV merge of (m, d, o) partial states.
 //   prefill_kernel  ragged (causal) prefill.  One workgroup owns a tile of
 //                   query tokens x all G heads of one kv head (4 waves x 64
@@ -1562,6 +1566,17 @@ constexpr int kPrefillWaves = ATTN_SINK_PREFILL_WAVES;
 #endif
 constexpr int kDecodeWaves = ATTN_SINK_DECODE_WAVES;
 constexpr int kDecodeUnroll = ATTN_SINK_DECODE_UNROLL;
+// Unsplit decode (one chunk per sequence and kv head): 16 waves per
+// workgroup (one workgroup per CU at 128 VGPRs and 104 KB of LDS) split the
+// chunk's pages 16 ways and merge in LDS -- a split and its merge in a
+// single launch, with no partial state leaving the CU.  Splits across
+// workgroups would need a device-wide release between two XCDs' L2s to
+// merge in the same launch; 16 waves per workgroup instead cut the
+// unsplit decode of the B = 64 mixed-length workload from 117 to 107 us.
+#ifndef ATTN_SINK_DECODE_WAVES_UNSPLIT
+#define ATTN_SINK_DECODE_WAVES_UNSPLIT 16
+#endif
+constexpr int kDecodeWavesUnsplit = ATTN_SINK_DECODE_WAVES_UNSPLIT;
 
 // Launch the prefill kernel for (dtype, key source, output form): a 1-D grid
 // of query tiles x (sequence, kv head) pairs x key chunks.
@@ -1709,18 +1724,21 @@ int decode_paged_impl(const void* q, const void* k_cache, const void* v_cache,
   const dim3 grid(num_splits, num_kv_heads, batch);
   const float qk = sm_scale * kLog2e;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (dtype == ATTN_SINK_BF16)
-    hipLaunchKernelGGL((decode_kernel<DT_BF16, kDecodeWaves, kDecodeUnroll>), grid,
-                       dim3(64 * kDecodeWaves), 0, s, (const char*)q, (const char*)k_cache,
-                       (const char*)v_cache, page_table, kv_lens, sinks, max_pages_per_seq,
-                       num_pages, num_kv_heads, group_size, qk, num_splits, partial_m,
-                       partial_d, partial_o, (char*)out);
-  else
-    hipLaunchKernelGGL((decode_kernel<DT_F32, kDecodeWaves, kDecodeUnroll>), grid,
-                       dim3(64 * kDecodeWaves), 0, s, (const char*)q, (const char*)k_cache,
-                       (const char*)v_cache, page_table, kv_lens, sinks, max_pages_per_seq,
-                       num_pages, num_kv_heads, group_size, qk, num_splits, partial_m,
-                       partial_d, partial_o, (char*)out);
+#define ATTN_SINK_DECODE(DTV, WV, UV)                                                          \
+  hipLaunchKernelGGL((decode_kernel<DTV, WV, UV>), grid, dim3(64 * (WV)), 0, s,                 \
+                     (const char*)q, (const char*)k_cache, (const char*)v_cache, page_table,   \
+                     kv_lens, sinks, max_pages_per_seq, num_pages, num_kv_heads, group_size,   \
+                     qk, num_splits, partial_m, partial_d, partial_o, (char*)out)
+  // (fp32 page fragments are twice as large: at 16 waves, 128 VGPRs hold one
+  // page group in flight per wave, not two)
+  if (dtype == ATTN_SINK_BF16) {
+    if (num_splits == 1) ATTN_SINK_DECODE(DT_BF16, kDecodeWavesUnsplit, kDecodeUnroll);
+    else ATTN_SINK_DECODE(DT_BF16, kDecodeWaves, kDecodeUnroll);
+  } else {
+    if (num_splits == 1) ATTN_SINK_DECODE(DT_F32, kDecodeWavesUnsplit, 1);
+    else ATTN_SINK_DECODE(DT_F32, kDecodeWaves, kDecodeUnroll);
+  }
+#undef ATTN_SINK_DECODE
   return launch_status();
 }
 
