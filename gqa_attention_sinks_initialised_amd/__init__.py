@@ -343,12 +343,13 @@ def attn_sink_decode_paged_static(q, k_cache, v_cache, page_table, kv_lens, sink
 
 def default_num_splits(kv_lens_host, num_kv_heads: int, cus: int = 256) -> int:
     """Split count for paged decode: enough (sequence, kv head, chunk) work
-    items for several waves of workgroups per compute unit."""
+    items for about six workgroups per compute unit (three rounds of the two
+    8-wave split-decode workgroups a CU holds), so that a chunk stays long."""
     b = len(kv_lens_host)
     if b == 0:
         return 1
     items = b * num_kv_heads
-    target = 8 * cus
+    target = 6 * cus
     s = max(1, -(-target // items))
     max_pages = max(1, max((int(L) + PAGE_SIZE - 1) // PAGE_SIZE for L in kv_lens_host))
     return int(min(s, max_pages, 256))

@@ -216,8 +216,9 @@ struct DecodeFrag<DT_F32> {
   u32x4 v[4];  // Vt[16j + l%16][4g .. 4g+3]
 };
 
-// Four bf16 decode waves per SIMD (at most 128 VGPRs): four workgroups per
-// compute unit keep more pages in flight.
+// Four bf16 decode waves per SIMD (at most 128 VGPRs), 16 per CU: two 8-wave
+// split-decode workgroups or one 16-wave unsplit one keep that many pages in
+// flight.
 #ifndef ATTN_SINK_DECODE_MIN_WAVES
 #define ATTN_SINK_DECODE_MIN_WAVES 4
 #endif
@@ -1556,10 +1557,12 @@ int launch_status() {
 #endif
 constexpr int kPrefillWaves = ATTN_SINK_PREFILL_WAVES;
 
-// Decode workgroup shape: waves per workgroup and pages per register group
-// (two groups are in flight per wave).
+// Split decode workgroup shape: waves per workgroup and pages per register
+// group (two groups are in flight per wave).  Eight waves (two workgroups per
+// CU at 128 VGPRs): the B = 64 mixed-length decode at 3 splits + merge runs
+// 102.7-103.1 us against 104.5-105.4 with four waves.
 #ifndef ATTN_SINK_DECODE_WAVES
-#define ATTN_SINK_DECODE_WAVES 4
+#define ATTN_SINK_DECODE_WAVES 8
 #endif
 #ifndef ATTN_SINK_DECODE_UNROLL
 #define ATTN_SINK_DECODE_UNROLL 2

@@ -221,10 +221,13 @@ def test_one_hot_retrieval_is_bit_exact(lib, dtype, splits):
             assert torch.equal(out[b, h], vs[b][t, h // (hq // hkv)]), (b, h)
 
 
-def test_decode_deterministic(lib):
+@pytest.mark.parametrize("splits", [1, 5])
+def test_decode_deterministic(lib, splits):
+    """Split decode + merge and the single launch (whose waves merge in LDS)
+    both reduce in a fixed order."""
     d = _to_dev(workloads.decode_inputs([900, 33, 4000], hq=16, hkv=2, seed=3))
-    a, _ = run_decode(lib, d, 5)
-    b, _ = run_decode(lib, d, 5)
+    a, _ = run_decode(lib, d, splits)
+    b, _ = run_decode(lib, d, splits)
     assert torch.equal(a, b)
 
 

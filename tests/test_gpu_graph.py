@@ -30,9 +30,9 @@ def _dev(d):
 
 
 def test_capture_and_replay_matches_eager_and_oracle(lib):
-    """Prefill + split decode + merge + split chunked (paged) prefill + merge,
-    captured once: every replay gives the eager bits, and those match the
-    oracle."""
+    """Prefill + split decode + merge + single-launch (unsplit) decode + split
+    chunked (paged) prefill + merge, captured once: every replay gives the
+    eager bits, and those match the oracle."""
     p = _dev(workloads.prefill_inputs([300, 77], hq=16, hkv=2, dtype=BF16, seed=3,
                                       sink_std=1.5))
     dh = workloads.decode_inputs([900, 33, 4000], hq=16, hkv=2, dtype=BF16, seed=4,
@@ -41,6 +41,7 @@ def test_capture_and_replay_matches_eager_and_oracle(lib):
     S = 7
     out_p = torch.empty_like(p["q"])
     out_d = torch.empty_like(d["q"])
+    out_d1 = torch.empty_like(d["q"])
     f32 = dict(device=DEV, dtype=torch.float32)
     pm = torch.empty((3, 16, S), **f32)
     pd = torch.empty((3, 16, S), **f32)
@@ -64,6 +65,9 @@ def test_capture_and_replay_matches_eager_and_oracle(lib):
                                    d["kv_lens"], d["sinks"], d["group"], d["sm_scale"], S,
                                    partial_m=pm, partial_d=pd, partial_o=po)
         lib.attn_sink_merge(pm, pd, po, out=out_d)
+        lib.attn_sink_decode_paged(d["q"], d["k_cache"], d["v_cache"], d["page_table"],
+                                   d["kv_lens"], d["sinks"], d["group"], d["sm_scale"], 1,
+                                   out=out_d1)
         lib.attn_sink_prefill_paged(c["q"], c["k_cache"], c["v_cache"], c["page_table"],
                                     c["cu_seqlens_q"], c["kv_lens"], c["sinks"], 40, c["group"],
                                     c["sm_scale"], True, num_splits=SC, partial_m=cm,
@@ -77,13 +81,15 @@ def test_capture_and_replay_matches_eager_and_oracle(lib):
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     ref_p, ref_d, ref_c = out_p.clone(), out_d.clone(), out_c.clone()
+    ref_d1 = out_d1.clone()
     ph = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in p.items()}
     assert_close(ref_p.cpu(), oracle.prefill(ph["q"], ph["k"], ph["v"], ph["sinks"],
                                              ph["cu_seqlens_q"], ph["cu_seqlens_kv"], 2, 8,
                                              ph["sm_scale"], True), BF16, "eager prefill")
-    assert_close(ref_d.cpu(), oracle.decode_paged(dh["q"], dh["k_cache"], dh["v_cache"],
-                                                  dh["page_table"], dh["kv_lens"], dh["sinks"],
-                                                  8, dh["sm_scale"]), BF16, "eager decode")
+    ref_dec = oracle.decode_paged(dh["q"], dh["k_cache"], dh["v_cache"], dh["page_table"],
+                                  dh["kv_lens"], dh["sinks"], 8, dh["sm_scale"])
+    assert_close(ref_d.cpu(), ref_dec, BF16, "eager decode")
+    assert_close(ref_d1.cpu(), ref_dec, BF16, "eager single-launch decode")
     assert_close(ref_c.cpu(), oracle.prefill_paged(ch["q"], ch["k_cache"], ch["v_cache"],
                                                    ch["page_table"], ch["cu_seqlens_q"],
                                                    ch["kv_lens"], ch["sinks"], 8,
@@ -95,6 +101,7 @@ def test_capture_and_replay_matches_eager_and_oracle(lib):
     for i in range(4):
         out_p.fill_(NAN)
         out_d.fill_(NAN)
+        out_d1.fill_(NAN)
         out_c.fill_(NAN)
         pm.fill_(NAN)
         cm.fill_(NAN)
@@ -103,11 +110,12 @@ def test_capture_and_replay_matches_eager_and_oracle(lib):
         torch.cuda.synchronize()
         assert torch.equal(out_p, ref_p), "prefill replay %d" % i
         assert torch.equal(out_d, ref_d), "decode+merge replay %d" % i
+        assert torch.equal(out_d1, ref_d1), "single-launch decode replay %d" % i
         assert torch.equal(out_c, ref_c), "chunked prefill+merge replay %d" % i
         path()                       # eager work between replays
         torch.cuda.synchronize()
         assert torch.equal(out_p, ref_p) and torch.equal(out_d, ref_d)
-        assert torch.equal(out_c, ref_c)
+        assert torch.equal(out_c, ref_c) and torch.equal(out_d1, ref_d1)
 
 
 @pytest.mark.parametrize("bucket", [128, 256])

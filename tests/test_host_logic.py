@@ -4,9 +4,10 @@ import gqa_attention_sinks_initialised_amd as m
 
 def test_decode_splits_fill_the_gpu():
     # 64 sequences x 8 kv heads = 512 items: 4 splits give 2048 = 8 per CU
-    assert m.default_num_splits([4096] * 64, 8) == 4
-    # few long sequences split up to the 256 cap
-    assert m.default_num_splits([131072] * 4, 8) == 64
+    assert m.default_num_splits([4096] * 64, 8) == 3
+    # few long sequences split into many chunks (up to the 256 cap)
+    assert m.default_num_splits([131072] * 4, 8) == 48
+    assert m.default_num_splits([131072], 1) == 256
     # never more splits than pages
     assert m.default_num_splits([20], 1) == 2
     assert m.default_num_splits([], 8) == 1
