@@ -176,6 +176,11 @@ int attn_sink_prefill_paged(const void *q, const void *k_cache,
  *              [c*ppc*16, min((c+1)*ppc*16, kv_len)).  Chunk 0 carries the
  *              sink; an empty chunk c > 0 yields (m, d, o) = (-inf, 0, 0).
  *   S == 1:    writes out [batch, Hkv*G, D] dtype; partials may be NULL.
+ *              One launch: the workgroup of a (sequence, kv head) splits
+ *              its pages over 16 waves and merges their states in LDS, so
+ *              no partial state is written and no merge call is needed
+ *              ("CuTeDSL at Perplexity", section "Grid synchronization",
+ *              weighs a merge in the same launch against a second one).
  *   k_cache and v_cache may be NULL when num_pages == 0.
  *   S  > 1:    writes partial_m, partial_d [batch, Hkv*G, S] and
  *              partial_o [batch, Hkv*G, S, D] (fp32; m in natural-log
