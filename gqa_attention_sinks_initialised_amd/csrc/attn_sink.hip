@@ -1761,8 +1761,16 @@ int merge_impl(const float* partial_m, const float* partial_d, const float* part
   if (rows == 0) return ATTN_SINK_OK;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const bool bf = out_dtype == ATTN_SINK_BF16;
-  // chunk lanes per row: up to 16, fewer when there are fewer splits
-  const int cl = num_splits >= 16 ? 16 : num_splits >= 8 ? 8 : num_splits >= 4 ? 4 : 2;
+  // Chunk lanes per row: the fewest that hold every chunk in registers (8
+  // per thread), so that many rows take few workgroups -- each round of
+  // workgroups costs one memory round trip -- but doubled while that leaves
+  // fewer than about two workgroups per CU.  32768 rows in 4 splits: 10.5 us
+  // with one lane per row against 17.6 with four; 4096 rows in 16 splits:
+  // 8.0 against 11.4 with sixteen.  Past 128 chunks, 16 lanes and a second
+  // loop.
+  int cl = num_splits <= 8 ? 1 : num_splits <= 16 ? 2 : num_splits <= 32 ? 4
+           : num_splits <= 64 ? 8 : 16;
+  while (cl < 16 && rows * cl / 16 < 512) cl *= 2;
   const int rpb = 256 / (16 * cl);
   const dim3 grid((unsigned)((rows + rpb - 1) / rpb));
 #define ATTN_SINK_MERGE(CLV)                                                                  \
@@ -1773,7 +1781,8 @@ int merge_impl(const float* partial_m, const float* partial_d, const float* part
     case 16: ATTN_SINK_MERGE(16); break;
     case 8: ATTN_SINK_MERGE(8); break;
     case 4: ATTN_SINK_MERGE(4); break;
-    default: ATTN_SINK_MERGE(2); break;
+    case 2: ATTN_SINK_MERGE(2); break;
+    default: ATTN_SINK_MERGE(1); break;
   }
 #undef ATTN_SINK_MERGE
   return launch_status();
