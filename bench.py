@@ -203,7 +203,7 @@ def main():
         attn.attn_sink_decode_paged(c3["q"], c3["k_cache"], c3["v_cache"], c3["page_table"],
                                     c3["kv_lens"], c3["sinks"], 8, c3["sm_scale"], 1, out=o3s)
 
-    # NEXT-row workloads: the prefill workload with its keys in a paged cache,
+    # Further workloads: the prefill workload with its keys in a paged cache,
     # and chunked prefill (few query tiles, long paged cache) unsplit and split.
     pk2 = workloads.pack_paged(c2["k"], c2["v"], c2["lens_kv"], seed=2002)
     out2p = torch.empty_like(c2["q"])
